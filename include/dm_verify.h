@@ -1,0 +1,148 @@
+/*
+ * dm_verify.h -- C ABI of the DropMatch verify-step library (libdmverify.so),
+ * hand-written HIP kernels for MI355X (gfx950).
+ *
+ * One call verifies the gamma drafted tokens of each of B sequences.  For each
+ * of the gamma+1 positions t of sequence b it runs the LM head on the target's
+ * last hidden state h[b, t, :], then applies that sequence's acceptance rule,
+ * scans the drafts left to right and emits one target token.
+ *
+ * What the call computes (sources: "Training-free Dropout Sampling for
+ * Semantic Token Acceptance in Speculative Decoding" (DropMatch), Sec. 3.1
+ * Eq. (1)-(3) and Sec. 3.2 Eq. (4)-(7), Algorithm 1; "Speculative Decoding:
+ * Draft, Then Verify", sections "The draft-then-verify loop", "The acceptance
+ * rule", "Greedy decoding"; "Why speculative decoding preserves distributions
+ * but may not be faster", Sec. 2 and the verify-round pseudocode of Sec. 5):
+ *
+ *   Lossy sequences (DM_MODE_NAIVE, DM_MODE_JS_MAJORITY), each position t:
+ *     keep[i, j] = Philox word (j/4, b*(gamma+1)+t, i, 0)[j%4] >= T,
+ *                  T = min(floor(p_drop * 2^32 + 1/2), 2^32 - 1)  (Eq. (1))
+ *     l^(i)[v]  = s * sum_j W[v, j] * h[b, t, j] * keep[i, j],
+ *                 s = 1 / (1 - p_drop), i = 0..K-1             (Eq. (2)-(3))
+ *     y^(i)     = argmax_v l^(i)[v] (smallest v on ties)
+ *     l-bar     = (1/K) sum_i l^(i); p-bar = softmax(l-bar)      (Eq. (5))
+ *   NAIVE:   accept draft x_t iff x_t is one of the y^(i)          (Eq. (4))
+ *   JS:      accept iff JS(q_hat_t || p-bar) <= max_i JS(p^(i) || p-bar)
+ *            (natural log, Eq. (6)), else iff more than K/2 heads give x_t
+ *            (Eq. (7)), else reject                         (Algorithm 1)
+ *   Emitted token: argmax of p-bar at the first rejected position A
+ *            (A = gamma when all drafts pass).
+ *
+ *   Lossless sequences (DM_MODE_LOSSLESS): one undropped row per position,
+ *     p_t = softmax(W h[b, t]).  With u_t = (Philox word (0, b*(gamma+1)+t,
+ *     0, 1)[0] >> 8) * 2^-24, accept x_t iff u_t * q_hat_t(x_t) < p_t(x_t)
+ *     (the min(1, p/q) test).  After a rejection at A the emitted token is
+ *     drawn from (p_A - q_hat_A)+ (p_A if that is zero everywhere); when all
+ *     pass, from p_gamma.  The draw is an exponential race: the winner
+ *     maximises w_v / (-ln U_v), U_v = ((Philox word (v/4, b*(gamma+1)+A, 0,
+ *     2)[v%4] >> 9) + 1/2) * 2^-23, ties to the smallest v.
+ *
+ *   Philox is Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed
+ *   (low word first).  A draft id outside [0, vocab) is rejected.
+ *
+ * Precision: bf16 (or fp32) inputs, fp32 accumulation and statistics.
+ *
+ * Memory: every pointer in dm_verify_args is DEVICE memory owned by the
+ * caller, except `modes`, which is HOST memory (the host needs the mode mix to
+ * lay out the LM-head rows).  The handle owns only its device workspace.
+ *
+ * Streams: dm_verify_run only enqueues work on `stream` (a hipStream_t; NULL
+ * means the null stream) and returns; outputs are valid once the stream has
+ * been synchronised.  One run may be in flight per handle at a time.
+ *
+ * Errors: every function returns a dm_status.  Argument checks happen on the
+ * host before any HIP call; a HIP failure maps to DM_ERR_HIP.
+ */
+#ifndef DM_VERIFY_H
+#define DM_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dm_status {
+    DM_OK = 0,
+    DM_ERR_INVALID_ARGUMENT = 1, /* NULL where required, value out of range */
+    DM_ERR_UNSUPPORTED = 2,      /* valid but not handled: dtype, d % 64, alignment */
+    DM_ERR_HIP = 3,              /* a HIP runtime call or a launch failed */
+    DM_ERR_OUT_OF_MEMORY = 4     /* workspace allocation failed */
+} dm_status;
+
+typedef enum dm_dtype { DM_DTYPE_F32 = 0, DM_DTYPE_BF16 = 1 } dm_dtype;
+
+typedef enum dm_mode {
+    DM_MODE_LOSSLESS = 0,    /* classical min(1, p/q) test, (p - q)+ residual */
+    DM_MODE_NAIVE = 1,       /* DropMatch naive token matching, Eq. (4) */
+    DM_MODE_JS_MAJORITY = 2  /* DropMatch Algorithm 1, Eq. (6) then Eq. (7) */
+} dm_mode;
+
+/* Problem limits fixed at handle creation. */
+typedef struct dm_verify_desc {
+    int32_t d;         /* hidden size; multiple of 64, 64..65536 */
+    int32_t vocab;     /* |V|, 1..2^24 */
+    int32_t max_batch; /* largest B a run may pass, 1..256 */
+    int32_t gamma;     /* drafted tokens per sequence, 0..31 (gamma+1 positions) */
+    int32_t k_max;     /* largest K a run may pass, 1..16 */
+    int32_t dtype;     /* dm_dtype of W and h */
+} dm_verify_desc;
+
+/* One verify step.  Shapes use the desc's d, vocab, gamma and this B, K. */
+typedef struct dm_verify_args {
+    const void* W;          /* device [vocab, d] row-major, dtype; 16-byte aligned */
+    const void* h;          /* device [B, gamma+1, d] row-major, dtype; 16-byte aligned */
+    const int32_t* draft;   /* device [B, gamma] drafted token ids (may be NULL iff gamma == 0) */
+    const float* q_hat;     /* device [B, gamma, vocab] draft distributions, used as given;
+                               required iff a sequence is LOSSLESS or JS_MAJORITY */
+    const uint8_t* modes;   /* HOST [B] dm_mode per sequence */
+    int32_t batch;          /* B, 1..max_batch */
+    int32_t K;              /* dropout heads for lossy sequences, 1..k_max */
+    float p_drop;           /* dropout probability, 0 <= p_drop < 1 */
+    uint32_t reserved;      /* must be 0 */
+    uint64_t seed;          /* Philox key */
+    int32_t* accept_len;    /* device out [B]: A, drafts accepted before the first rejection */
+    int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
+    /* Optional device outputs for inspection; NULL = not written. */
+    uint8_t* accept_flags;     /* [B, gamma] decision at every drafted position */
+    int32_t* head_argmax;      /* [B, gamma+1, K]; -1 in heads 1.. of lossless sequences */
+    int32_t* centroid_argmax;  /* [B, gamma+1]; the undropped argmax for lossless sequences */
+    float* head_logz;          /* [B, gamma+1, K] log partition of each head row */
+    float* centroid_logz;      /* [B, gamma+1] */
+    float* js_heads;           /* [B, gamma, K] JS(p^(i) || p-bar), JS_MAJORITY sequences only */
+    float* js_draft;           /* [B, gamma] JS(q_hat || p-bar), JS_MAJORITY sequences only */
+    float* logits;             /* [B, gamma+1, K, vocab] every row, fp32 (lossless: head 0) */
+    uint32_t* mask_bits;       /* [B, gamma+1, K, d/32] keep bits, bit j%32 of word j/32
+                                  (lossless: all ones in head 0) */
+} dm_verify_args;
+
+typedef struct dm_verify dm_verify_t; /* opaque */
+
+/* Validates `desc`, allocates the device workspace on the current device.
+ * *out receives the handle (NULL on failure). */
+int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out);
+
+/* Enqueues one verify step on `stream` (hipStream_t, NULL = null stream).
+ * Validates every argument first; returns without enqueuing on error. */
+int dm_verify_run(dm_verify_t* handle, const dm_verify_args* args, void* stream);
+
+/* Frees the workspace and the handle.  NULL is a no-op returning DM_OK. */
+int dm_verify_destroy(dm_verify_t* handle);
+
+/* Host-only checks, no HIP call: the validation dm_verify_create and
+ * dm_verify_run perform, usable without a GPU.  `args` may be NULL to check
+ * only `desc`. */
+int dm_verify_check(const dm_verify_desc* desc, const dm_verify_args* args);
+
+/* Device bytes the workspace of `desc` occupies (0 when desc is invalid). */
+size_t dm_verify_workspace_bytes(const dm_verify_desc* desc);
+
+/* Static description of a status code. */
+const char* dm_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DM_VERIFY_H */

@@ -102,11 +102,12 @@ double dmo_accept_uniform(uint64_t seed, uint32_t pidx)
 }
 
 /* Race uniform for vocabulary entry v at position index pidx.
- * Stream 2: counter (v/4, pidx, 0, 2), word v%4; 24 bits -> (0, 1). */
+ * Stream 2: counter (v/4, pidx, 0, 2), word v%4; the top 23 bits plus one
+ * half, times 2^-23, give a value in (0, 1) that fp32 holds exactly. */
 double dmo_race_uniform(uint64_t seed, uint32_t pidx, uint32_t v)
 {
     uint32_t r = philox_word(seed, v >> 2, pidx, 0u, 2u, (int)(v & 3u));
-    return ((double)(r >> 8) + 0.5) * (1.0 / 16777216.0);
+    return ((double)(r >> 9) + 0.5) * (1.0 / 8388608.0);
 }
 
 static double decode(const void* base, int dtype, size_t idx)

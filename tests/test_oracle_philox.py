@@ -137,4 +137,5 @@ def test_streams_are_distinct():
     for u in u_acc:
         assert (u * 2**24) == int(u * 2**24)
     for u in u_race:
-        assert (u * 2**24 - 0.5) == int(u * 2**24 - 0.5)
+        assert (u * 2**23 - 0.5) == int(u * 2**23 - 0.5)
+        assert float(np.float32(u)) == u  # exact in fp32
