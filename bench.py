@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of the DropMatch verify step on one MI355X.
+
+One step = one dm_verify_run over a batch of synthetic inputs already
+resident in HBM: masks, the K-head LM head, statistics, JS terms, the rules,
+the scan and the emitted token.  Prints one JSON line on stdout.
+
+  python bench.py [--steps K] [--warmup W] [--config C]
+
+The default workload is the Llama-3-8B-shaped head (B = 1, gamma = 7,
+d = 4096, |V| = 128256, K = 5, p_drop = 0.2, JS + majority).  --config picks
+another of the five workloads for inspection.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_philox_amd", "csrc", "dm_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"k_gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seed, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    B = w.cfg.B
+    done_pos, elapsed, calls = 0, 0.0, 0
+    b = 0
+    while elapsed < budget_s and calls < B:
+        t0 = time.perf_counter()
+        oracle.run(w.W, w.h, w.draft, w.q_hat, w.modes, w.K, w.p_drop, seed, seqs=np.array([b], np.int32),
+                   n_threads=threads)
+        elapsed += time.perf_counter() - t0
+        done_pos += w.cfg.gamma + 1
+        calls += 1
+        b += 1
+    return {"value": done_pos / elapsed, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} sequence(s) x {w.cfg.gamma + 1} positions of the same workload, fp64, "
+                      f"{elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--p-drop", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this verify step is built and measured on a single MI355X "
+              "(--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verification_philox_amd import binding as Bd
+    from speculative_decoding_verification_philox_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = wl.CONFIGS[args.config]
+    over = {}
+    if args.p_drop is not None:
+        over["p_drop"] = args.p_drop
+    t0 = time.perf_counter()
+    w = wl.generate(cfg, **over)
+    cfg = w.cfg
+    log(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f} s")
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    W, h = dev_t(w.W), dev_t(w.h)
+    draft = dev_t(w.draft.astype(np.int32))
+    q_hat = dev_t(w.q_hat)
+    dtype_code = Bd.DM_DTYPE_BF16 if cfg.dtype == wl.DTYPE_BF16 else Bd.DM_DTYPE_F32
+    ver = Bd.Verifier(d=cfg.d, vocab=cfg.V, max_batch=cfg.B, gamma=cfg.gamma, k_max=cfg.K, dtype=dtype_code)
+    seed = wl.perf_seed(cfg.index)
+    outs = {"accept_len": torch.empty(cfg.B, dtype=torch.int32, device=dev),
+            "out_token": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ver.run(W, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=stream.cuda_stream, outputs=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    gemm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        Bd.dm_verify_profile(ver.handle, gemm_ev[i][0].cuda_event, gemm_ev[i][1].cuda_event)
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    gemm_ms = [a.elapsed_time(b) for a, b in gemm_ev]
+    gemm_avg = float(np.mean(gemm_ms))
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), wall {wall / args.steps * 1e6:.1f} us/step; "
+        f"GEMM kernel {gemm_avg * 1e3:.1f} us avg, min {min(gemm_ms) * 1e3:.1f} us")
+
+    positions = cfg.B * (cfg.gamma + 1)
+    value = positions / (ms_step / 1e3)
+    n_lossless = int((w.modes == wl.LOSSLESS).sum())
+    rows = (cfg.B - n_lossless) * (cfg.gamma + 1) * cfg.K + n_lossless * (cfg.gamma + 1)
+    elem = 2 if cfg.dtype == wl.DTYPE_BF16 else 4
+    alg_bytes = cfg.V * cfg.d * elem + positions * cfg.d * elem
+    alg_flops = 2.0 * rows * cfg.d * cfg.V
+    intensity = alg_flops / alg_bytes
+    dname = "bf16" if cfg.dtype == wl.DTYPE_BF16 else "f32"
+    balance = MFMA_PEAK_TFLOPS[dname] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < balance:
+        achieved = alg_bytes / (gemm_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg_flops / (gemm_avg / 1e3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dname]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    roof["kernel"] = "k_gemm_skinny"
+    roof["traffic"] = measured_traffic(cfg.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores ...")
+        cpu = cpu_baseline(w, seed, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.3f} positions/s on {cpu['cores']} threads")
+
+    modes_desc = {"js": "JS+majority", "naive": "naive", "lossless": "lossless",
+                  "half_lossless_naive": "half lossless / half naive"}[cfg.modes]
+    line = {
+        "metric": "verified positions/sec (K=5 dropout heads + accept) and % HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dname,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={cfg.B}, gamma={cfg.gamma}, d={cfg.d}, |V|={cfg.V}, K={cfg.K}, "
+                               f"p_drop={cfg.p_drop}, {modes_desc}",
+                   "batch": cfg.B, "positions_per_step": positions, "gemm_rows": rows},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    ver.close()
+
+
+if __name__ == "__main__":
+    main()

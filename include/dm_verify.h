@@ -130,6 +130,12 @@ int dm_verify_run(dm_verify_t* handle, const dm_verify_args* args, void* stream)
 /* Frees the workspace and the handle.  NULL is a no-op returning DM_OK. */
 int dm_verify_destroy(dm_verify_t* handle);
 
+/* For measurement tools: arms `handle` so that its next dm_verify_run records
+ * `start` (a hipEvent_t) on the run's stream right before the LM-head GEMM
+ * kernel and `stop` right after it; the run then disarms it.  Either event
+ * may be NULL to disarm.  The events stay owned by the caller. */
+int dm_verify_profile(dm_verify_t* handle, void* start, void* stop);
+
 /* Host-only checks, no HIP call: the validation dm_verify_create and
  * dm_verify_run perform, usable without a GPU.  `args` may be NULL to check
  * only `desc`. */

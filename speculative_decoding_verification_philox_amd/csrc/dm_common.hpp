@@ -1,0 +1,237 @@
+// dm_common.hpp -- internal definitions shared by the host side and the
+// kernels of libdmverify: the per-call plan, the LM-head row layout, the
+// device Philox4x32-10, and softmax-statistic merging.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmv {
+
+constexpr int kMaxBatch = 256;
+constexpr int kMaxK = 16;
+constexpr int kMaskWords = kMaxBatch / 32;
+
+enum Mode : int { kLossless = 0, kNaive = 1, kJs = 2 };
+
+// Row layout of the LM-head GEMM ("slot layout").
+//
+// The GEMM's M dimension is cut into tiles of MT rows.  Inside a tile the
+// MFMA output layout gives each lane `GR` row groups; a lane holds the rows of
+// one group for one vocabulary column.  Each group has S row slots, and a
+// position occupies K consecutive slots of one group (one per dropout head),
+// so every head of a position lands in the same lane as its siblings.  Lossy
+// positions fill tiles first (ppg = S / K per group), lossless positions
+// (one undropped row each) fill the tiles after them.
+//
+// geom 0: 16x16 MFMA output, a tile is MT = 16 * msub rows, GR = 4 groups,
+//         row r of the tile = 16 m + 4 g + j  (slot lambda = 4 m + j).
+// geom 1: 32x32 MFMA output, a tile is MT = 32 * msub rows, GR = 2 groups,
+//         row r = 32 m + 8 a + 4 g + c        (slot lambda = 16 m + 4 a + c).
+struct Plan {
+    // problem
+    int B, T1, G, K, V, d;
+    int dtype;           // 0 f32, 1 bf16
+    float scale;         // 1 / (1 - p_drop)
+    uint32_t thresh;     // keep iff Philox word >= thresh
+    uint32_t key0, key1; // Philox key (seed low, high)
+    // sequences
+    uint32_t lossless_bits[kMaskWords];
+    uint32_t js_bits[kMaskWords];
+    int n_lossy_seq, n_lossless_seq, n_js_seq;
+    // slot layout
+    int geom, msub, MT, GR, S;
+    int ppg;                // lossy positions per group (S / K)
+    int n_lossy_pos, n_lossless_pos;
+    int tiles_lossy, n_tiles, R_phys;
+    // stored logits: rows of [B * T1 * K, V]
+    int store_all;
+    // vocabulary split of the GEMM's statistic partials
+    int n_vgroups;
+    // JS pass
+    int n_js_pos, js_chunks, js_chunk;
+    // residual race
+    int race_chunks, race_chunk;
+};
+
+// ------------------------------------------------------------------ layout
+__host__ __device__ inline bool bit_of(const uint32_t* bits, int b) {
+    return (bits[b >> 5] >> (b & 31)) & 1u;
+}
+
+// Number of set bits of `bits` below position b (or of clear bits, for the
+// complement set), within [0, B).
+__host__ __device__ inline int rank_of(const uint32_t* bits, int b, bool set) {
+    int r = 0;
+    for (int w = 0; w < (b >> 5); ++w) {
+        uint32_t x = set ? bits[w] : ~bits[w];
+        r += __builtin_popcount(x);
+    }
+    uint32_t x = set ? bits[b >> 5] : ~bits[b >> 5];
+    uint32_t below = (b & 31) ? (x & ((1u << (b & 31)) - 1u)) : 0u;
+    return r + __builtin_popcount(below);
+}
+
+// The sequence index of the `rank`-th member of the set (set bits when `set`,
+// clear bits otherwise) among sequences [0, B); -1 if there is none.
+__host__ __device__ inline int select_of(const uint32_t* bits, int B, int rank, bool set) {
+    for (int b = 0; b < B; ++b) {
+        if (bit_of(bits, b) == set) {
+            if (rank == 0) return b;
+            --rank;
+        }
+    }
+    return -1;
+}
+
+__host__ __device__ inline int tile_row(int geom, int g, int lambda) {
+    if (geom == 0) return 16 * (lambda >> 2) + 4 * g + (lambda & 3);
+    return 32 * (lambda >> 4) + 8 * ((lambda & 15) >> 2) + 4 * g + (lambda & 3);
+}
+
+__host__ __device__ inline void tile_slot(int geom, int r, int* g, int* lambda) {
+    if (geom == 0) {
+        *g = (r & 15) >> 2;
+        *lambda = 4 * (r >> 4) + (r & 3);
+    } else {
+        int rr = r & 31;
+        *g = (rr & 7) >> 2;
+        *lambda = 16 * (r >> 5) + 4 * (rr >> 3) + (rr & 3);
+    }
+}
+
+// What a physical GEMM row holds.
+struct RowInfo {
+    int b, t, i;   // sequence, position, head; b < 0 for a padding row
+    int lossy;     // 1 if the row is masked and scaled
+    int lossy_pos; // index of the lossy position (centroid slot), -1 otherwise
+};
+
+__host__ __device__ inline RowInfo row_info(const Plan& P, int rho) {
+    RowInfo ri{-1, 0, 0, 0, -1};
+    int tile = rho / P.MT, r = rho - tile * P.MT;
+    int g, lam;
+    tile_slot(P.geom, r, &g, &lam);
+    if (tile < P.tiles_lossy) {
+        int slot = lam / P.K;
+        if (slot >= P.ppg) return ri;
+        int p = (tile * P.GR + g) * P.ppg + slot;
+        if (p >= P.n_lossy_pos) return ri;
+        ri.b = select_of(P.lossless_bits, P.B, p / P.T1, false);
+        ri.t = p % P.T1;
+        ri.i = lam - slot * P.K;
+        ri.lossy = 1;
+        ri.lossy_pos = p;
+    } else {
+        int q = ((tile - P.tiles_lossy) * P.GR + g) * P.S + lam;
+        if (q >= P.n_lossless_pos) return ri;
+        ri.b = select_of(P.lossless_bits, P.B, q / P.T1, true);
+        ri.t = q % P.T1;
+        ri.i = 0;
+        ri.lossy = 0;
+    }
+    return ri;
+}
+
+// Physical row of head i of lossy position p.
+__host__ __device__ inline int lossy_row(const Plan& P, int p, int i) {
+    int grp = p / P.ppg, slot = p - grp * P.ppg;
+    int tile = grp / P.GR, g = grp - tile * P.GR;
+    return tile * P.MT + tile_row(P.geom, g, slot * P.K + i);
+}
+
+// Physical row of lossless position q.
+__host__ __device__ inline int lossless_row(const Plan& P, int q) {
+    int grp = q / P.S, lam = q - grp * P.S;
+    int tile = P.tiles_lossy + grp / P.GR, g = grp % P.GR;
+    return tile * P.MT + tile_row(P.geom, g, lam);
+}
+
+// ------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror, Shaw (SC'11): ten rounds; each round multiplies
+// counter words 0 and 2 by the two Philox multipliers, XORs the high halves
+// with the crossed counter words and the round key, and the key advances by
+// the two Weyl increments.
+struct u32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
+        uint32_t hi0 = __umulhi(m0, c.x), lo0 = m0 * c.x;
+        uint32_t hi1 = __umulhi(m1, c.z), lo1 = m1 * c.z;
+        c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Stream tags (counter word 3).
+constexpr uint32_t kStreamMask = 0u, kStreamAccept = 1u, kStreamRace = 2u;
+
+// ------------------------------------------------------------- statistics
+// Softmax statistics of a set of logits: running max m, s = sum exp(l - m)
+// and the smallest index attaining m.
+struct Stat {
+    float m;
+    float s;
+    int idx;
+};
+
+__device__ __forceinline__ Stat stat_empty() { return Stat{-INFINITY, 0.0f, 0x7fffffff}; }
+
+__device__ __forceinline__ void stat_push(Stat& a, float v, int idx) {
+    if (v > a.m) {
+        a.s = a.s * __expf(a.m - v) + 1.0f;
+        a.m = v;
+        a.idx = idx;
+    } else {
+        a.s += __expf(v - a.m);
+        if (v == a.m && idx < a.idx) a.idx = idx;
+    }
+}
+
+__device__ __forceinline__ Stat stat_merge(Stat a, Stat b) {
+    if (b.m == -INFINITY) return a;
+    if (a.m == -INFINITY) return b;
+    Stat r;
+    if (a.m > b.m) {
+        r.m = a.m;
+        r.s = a.s + b.s * __expf(b.m - a.m);
+        r.idx = a.idx;
+    } else if (b.m > a.m) {
+        r.m = b.m;
+        r.s = b.s + a.s * __expf(a.m - b.m);
+        r.idx = b.idx;
+    } else {
+        r.m = a.m;
+        r.s = a.s + b.s;
+        r.idx = a.idx < b.idx ? a.idx : b.idx;
+    }
+    return r;
+}
+
+// Final per-row statistics.
+struct RowStat {
+    float m;
+    float logz;
+    int idx;
+};
+
+// Mean of the K head logits of one position: the DropMatch centroid logit.
+// Every kernel that forms it goes through this function so the values agree
+// bit for bit.
+template <class Get>
+__device__ __forceinline__ float centroid_logit(int K, Get get) {
+    float s = get(0);
+    for (int i = 1; i < K; ++i) s += get(i);
+    return s / (float)K;
+}
+
+// ----------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+}  // namespace dmv

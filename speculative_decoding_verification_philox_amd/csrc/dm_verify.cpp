@@ -1,0 +1,327 @@
+// dm_verify.cpp -- host side of libdmverify: argument checks, the per-call
+// plan (row layout, work split), workspace, and the kernel sequence.
+#include "../../include/dm_verify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "dm_common.hpp"
+#include "dm_launch.hpp"
+
+using namespace dmv;
+
+struct dm_verify {
+    dm_verify_desc desc;
+    int device;
+    uint8_t* ws;
+    size_t ws_bytes;
+    void* Hm;
+    float* logits;
+    Stat* part;
+    RowStat* rowstat;
+    RowStat* centstat;
+    float* jspart;
+    unsigned long long* race;
+    hipEvent_t prof_start, prof_stop;
+};
+
+namespace {
+
+constexpr int kGroupsPerTile = 4;  // 16x16 MFMA output: four row groups per lane
+
+int elem_size(int dtype) { return dtype == DM_DTYPE_BF16 ? 2 : 4; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_desc(const dm_verify_desc* D) {
+    if (!D) return DM_ERR_INVALID_ARGUMENT;
+    if (D->d <= 0 || D->vocab <= 0 || D->max_batch <= 0 || D->gamma < 0 || D->k_max <= 0)
+        return DM_ERR_INVALID_ARGUMENT;
+    if (D->max_batch > kMaxBatch || D->gamma > 31 || D->k_max > kMaxK || D->vocab > (1 << 24))
+        return DM_ERR_INVALID_ARGUMENT;
+    if (D->dtype != DM_DTYPE_F32 && D->dtype != DM_DTYPE_BF16) return DM_ERR_UNSUPPORTED;
+    if (D->d % 64 != 0 || D->d > 65536) return DM_ERR_UNSUPPORTED;
+    return DM_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
+    if (!a) return DM_ERR_INVALID_ARGUMENT;
+    if (a->reserved != 0) return DM_ERR_INVALID_ARGUMENT;
+    if (a->batch < 1 || a->batch > D->max_batch) return DM_ERR_INVALID_ARGUMENT;
+    if (a->K < 1 || a->K > D->k_max) return DM_ERR_INVALID_ARGUMENT;
+    if (!(a->p_drop >= 0.0f && a->p_drop < 1.0f)) return DM_ERR_INVALID_ARGUMENT;
+    if (!a->W || !a->h || !a->modes || !a->accept_len || !a->out_token) return DM_ERR_INVALID_ARGUMENT;
+    if (D->gamma > 0 && !a->draft) return DM_ERR_INVALID_ARGUMENT;
+    bool need_q = false;
+    for (int b = 0; b < a->batch; ++b) {
+        uint8_t m = a->modes[b];
+        if (m > DM_MODE_JS_MAJORITY) return DM_ERR_INVALID_ARGUMENT;
+        if (m != DM_MODE_NAIVE) need_q = true;
+    }
+    if (need_q && D->gamma > 0 && !a->q_hat) return DM_ERR_INVALID_ARGUMENT;
+    if (!aligned(a->W, 16) || !aligned(a->h, 16)) return DM_ERR_UNSUPPORTED;
+    const void* four[] = {a->draft, a->q_hat, a->accept_len, a->out_token, a->head_argmax, a->centroid_argmax,
+                          a->head_logz, a->centroid_logz, a->js_heads, a->js_draft, a->logits, a->mask_bits};
+    for (const void* p : four)
+        if (p && !aligned(p, 4)) return DM_ERR_UNSUPPORTED;
+    return DM_OK;
+}
+
+uint32_t drop_threshold(float p_drop) {
+    // keep iff a 32-bit Philox word is >= T, so P(drop) = T / 2^32
+    double t = std::floor((double)p_drop * 4294967296.0 + 0.5);
+    if (t > 4294967295.0) t = 4294967295.0;
+    if (t < 0.0) t = 0.0;
+    return (uint32_t)t;
+}
+
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Row layout and work split of one call.
+void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, Plan& P) {
+    P.B = B;
+    P.T1 = D.gamma + 1;
+    P.G = D.gamma;
+    P.K = K;
+    P.V = D.vocab;
+    P.d = D.d;
+    P.dtype = D.dtype;
+    P.n_lossless_seq = n_lossless;
+    P.n_lossy_seq = B - n_lossless;
+    P.n_js_seq = n_js;
+    P.n_lossy_pos = P.n_lossy_seq * P.T1;
+    P.n_lossless_pos = n_lossless * P.T1;
+
+    // smallest number of tiles, then the fewest rows
+    P.geom = 0;
+    P.GR = kGroupsPerTile;
+    int best_ms = 0, best_tiles = 0;
+    for (int ms = 1; ms <= 4; ++ms) {
+        const int S = 4 * ms;
+        if (P.n_lossy_pos > 0 && S < K) continue;
+        const int ppg = S / K;
+        const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
+        const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
+        if (best_ms == 0 || tl + tn < best_tiles) {
+            best_ms = ms;
+            best_tiles = tl + tn;
+        }
+    }
+    P.msub = best_ms;
+    P.MT = 16 * best_ms;
+    P.S = 4 * best_ms;
+    P.ppg = P.n_lossy_pos > 0 ? P.S / K : 1;
+    P.tiles_lossy = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * P.ppg) : 0;
+    P.n_tiles = best_tiles;
+    P.R_phys = P.n_tiles * P.MT;
+
+    const int nstr = cdiv(P.V, 16);
+    const int spg = skinny_strips_per_group();
+    int ng = cdiv(nstr, spg);
+    const int fill = nstr < 256 ? nstr : 256;
+    P.n_vgroups = ng > fill ? ng : fill;
+
+    P.n_js_pos = n_js * P.G;
+    P.js_chunks = 1;
+    P.js_chunk = P.V;
+    if (P.n_js_pos > 0) {
+        int ch = cdiv(2048, P.n_js_pos);
+        const int chmax = cdiv(P.V, 256);
+        ch = ch < 1 ? 1 : (ch > chmax ? chmax : ch);
+        P.js_chunk = cdiv(cdiv(P.V, ch), 256) * 256;
+        P.js_chunks = cdiv(P.V, P.js_chunk);
+    }
+    P.race_chunks = 1;
+    P.race_chunk = P.V;
+    if (n_lossless > 0) {
+        int ch = cdiv(1024, n_lossless);
+        const int chmax = cdiv(P.V, 1024);
+        ch = ch < 1 ? 1 : (ch > chmax ? chmax : ch);
+        P.race_chunk = cdiv(cdiv(P.V, ch), 1024) * 1024;
+        P.race_chunks = cdiv(P.V, P.race_chunk);
+    }
+}
+
+struct Sizes {
+    size_t hm, logits, part, rowstat, centstat, jspart, race;
+};
+
+Sizes workspace_sizes(const dm_verify_desc& D) {
+    Sizes s{};
+    const size_t T1 = (size_t)D.gamma + 1;
+    size_t max_hm_rows = 0, max_part = 0, max_js = 0;
+    for (int K = 1; K <= D.k_max; ++K) {
+        for (int nl = 0; nl <= D.max_batch; ++nl) {
+            Plan P{};
+            make_plan(D, D.max_batch, K, nl, D.max_batch - nl, P);
+            if ((size_t)P.R_phys > max_hm_rows) max_hm_rows = P.R_phys;
+            size_t part = (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos);
+            if (part > max_part) max_part = part;
+            // JS positions can be any count up to max_batch * gamma
+        }
+    }
+    for (int nj = 1; nj <= D.max_batch; ++nj) {
+        for (int K = D.k_max; K <= D.k_max; ++K) {
+            Plan P{};
+            make_plan(D, D.max_batch, K, 0, nj, P);
+            size_t js = (size_t)P.n_js_pos * P.js_chunks * (K + 1);
+            if (js > max_js) max_js = js;
+        }
+    }
+    s.hm = max_hm_rows * (size_t)D.d * elem_size(D.dtype);
+    s.logits = (size_t)D.max_batch * T1 * D.k_max * D.vocab * sizeof(float);
+    s.part = max_part * sizeof(Stat);
+    s.rowstat = (size_t)D.max_batch * T1 * D.k_max * sizeof(RowStat);
+    s.centstat = (size_t)D.max_batch * T1 * sizeof(RowStat);
+    s.jspart = (max_js > 0 ? max_js : 1) * sizeof(float);
+    s.race = (size_t)D.max_batch * 2 * sizeof(unsigned long long);
+    return s;
+}
+
+size_t total_bytes(const Sizes& s) {
+    const size_t a = 256;
+    return align_up(s.hm, a) + align_up(s.logits, a) + align_up(s.part, a) + align_up(s.rowstat, a) +
+           align_up(s.centstat, a) + align_up(s.jspart, a) + align_up(s.race, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dm_verify_status_string(int status) {
+    switch (status) {
+        case DM_OK: return "ok";
+        case DM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case DM_ERR_UNSUPPORTED: return "unsupported";
+        case DM_ERR_HIP: return "HIP runtime error";
+        case DM_ERR_OUT_OF_MEMORY: return "out of device memory";
+        default: return "unknown status";
+    }
+}
+
+int dm_verify_check(const dm_verify_desc* desc, const dm_verify_args* args) {
+    int rc = check_desc(desc);
+    if (rc != DM_OK || !args) return rc;
+    return check_args(desc, args);
+}
+
+size_t dm_verify_workspace_bytes(const dm_verify_desc* desc) {
+    if (check_desc(desc) != DM_OK) return 0;
+    return total_bytes(workspace_sizes(*desc));
+}
+
+int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
+    if (!out) return DM_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    int rc = check_desc(desc);
+    if (rc != DM_OK) return rc;
+    dm_verify* h = new (std::nothrow) dm_verify();
+    if (!h) return DM_ERR_OUT_OF_MEMORY;
+    h->desc = *desc;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return DM_ERR_HIP;
+    }
+    const Sizes s = workspace_sizes(*desc);
+    h->ws_bytes = total_bytes(s);
+    hipError_t e = hipMalloc((void**)&h->ws, h->ws_bytes);
+    if (e != hipSuccess) {
+        delete h;
+        (void)hipGetLastError();
+        return e == hipErrorOutOfMemory ? DM_ERR_OUT_OF_MEMORY : DM_ERR_HIP;
+    }
+    uint8_t* p = h->ws;
+    auto take = [&](size_t n) {
+        uint8_t* r = p;
+        p += align_up(n, 256);
+        return r;
+    };
+    h->Hm = take(s.hm);
+    h->logits = (float*)take(s.logits);
+    h->part = (Stat*)take(s.part);
+    h->rowstat = (RowStat*)take(s.rowstat);
+    h->centstat = (RowStat*)take(s.centstat);
+    h->jspart = (float*)take(s.jspart);
+    h->race = (unsigned long long*)take(s.race);
+    *out = h;
+    return DM_OK;
+}
+
+int dm_verify_profile(dm_verify_t* h, void* start, void* stop) {
+    if (!h) return DM_ERR_INVALID_ARGUMENT;
+    h->prof_start = (start && stop) ? (hipEvent_t)start : nullptr;
+    h->prof_stop = (start && stop) ? (hipEvent_t)stop : nullptr;
+    return DM_OK;
+}
+
+int dm_verify_destroy(dm_verify_t* h) {
+    if (!h) return DM_OK;
+    int rc = DM_OK;
+    if (h->ws && hipFree(h->ws) != hipSuccess) rc = DM_ERR_HIP;
+    delete h;
+    return rc;
+}
+
+int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
+    if (!h) return DM_ERR_INVALID_ARGUMENT;
+    int rc = check_args(&h->desc, a);
+    if (rc != DM_OK) return rc;
+    const dm_verify_desc& D = h->desc;
+    hipStream_t st = (hipStream_t)stream;
+
+    Plan P{};
+    int n_lossless = 0, n_js = 0;
+    for (int b = 0; b < a->batch; ++b) {
+        n_lossless += a->modes[b] == DM_MODE_LOSSLESS;
+        n_js += a->modes[b] == DM_MODE_JS_MAJORITY;
+    }
+    make_plan(D, a->batch, a->K, n_lossless, n_js, P);
+    for (int b = 0; b < a->batch; ++b) {
+        if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
+        if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
+    }
+    P.scale = (float)(1.0 / (1.0 - (double)a->p_drop));
+    P.thresh = drop_threshold(a->p_drop);
+    P.key0 = (uint32_t)(a->seed & 0xffffffffu);
+    P.key1 = (uint32_t)(a->seed >> 32);
+    P.store_all = a->logits != nullptr;
+    float* logits = a->logits ? a->logits : h->logits;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return DM_ERR_HIP;
+
+    const int T1 = P.T1;
+    hipError_t e = hipSuccess;
+#define DM_TRY(x)                          \
+    do {                                   \
+        e = (x);                           \
+        if (e != hipSuccess) return DM_ERR_HIP; \
+    } while (0)
+    if (a->head_argmax) DM_TRY(launch_fill_i32(a->head_argmax, a->batch * T1 * a->K, -1, st));
+    if (a->mask_bits) DM_TRY(launch_fill_i32((int32_t*)a->mask_bits, a->batch * T1 * a->K * (D.d / 32), 0, st));
+    DM_TRY(launch_prep(P, a->h, h->Hm, a->mask_bits, st));
+    const bool prof = h->prof_start && h->prof_stop;
+    if (prof) DM_TRY(hipEventRecord(h->prof_start, st));
+    DM_TRY(launch_gemm(P, a->W, h->Hm, logits, h->part, st));
+    if (prof) {
+        DM_TRY(hipEventRecord(h->prof_stop, st));
+        h->prof_start = h->prof_stop = nullptr;
+    }
+    DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, a->head_argmax, a->head_logz, a->centroid_argmax,
+                          a->centroid_logz, st));
+    if (P.n_js_pos > 0) DM_TRY(launch_js(P, logits, a->q_hat, h->rowstat, h->centstat, h->jspart, st));
+    DM_TRY(launch_decide(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, a->accept_len,
+                         a->out_token, h->race, a->accept_flags, a->js_heads, a->js_draft, st));
+    if (P.n_lossless_seq > 0)
+        DM_TRY(launch_race(P, a->q_hat, logits, h->rowstat, a->accept_len, h->race, a->out_token, st));
+#undef DM_TRY
+    return DM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the oracle element by element.
+
+Parity bar (from the verify step's contract):
+  * dropout masks, argmaxes and emitted tokens bit-exact;
+  * logits within 2e-2 absolute, JS values within 1e-5 absolute;
+  * accept decisions identical except where the oracle's margin is below
+    1e-4 (such near-ties are counted and reported).
+An argmax (or emitted token) may differ only where the oracle's top-2 gap is
+below the same 1e-4 (the fp32 path cannot order closer values reliably);
+those are counted too.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import oracle
+from speculative_decoding_verification_philox_amd import binding as B
+from speculative_decoding_verification_philox_amd import workloads as wl
+
+LOGIT_TOL = 2e-2
+JS_TOL = 1e-5
+LOGZ_TOL = 1e-3
+MARGIN = 1e-4
+RACE_GAP = 1e-3
+
+
+def gpu_available():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def to_device(a: np.ndarray):
+    import torch
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class Inputs:
+    """Device copies of one workload's tensors."""
+
+    def __init__(self, W, h, draft, q_hat):
+        self.W = to_device(W)
+        self.h = to_device(h)
+        self.draft = to_device(np.ascontiguousarray(draft, dtype=np.int32))
+        self.q_hat = to_device(np.ascontiguousarray(q_hat, dtype=np.float32)) if q_hat is not None else None
+
+
+def make_verifier(W, h, K, max_batch=None):
+    V, d = W.shape
+    Bsz, T1, _ = h.shape
+    dtype = B.DM_DTYPE_BF16 if W.dtype == np.uint16 else B.DM_DTYPE_F32
+    return B.Verifier(d=d, vocab=V, max_batch=max_batch or Bsz, gamma=T1 - 1, k_max=max(K, 1), dtype=dtype)
+
+
+def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True):
+    import torch
+
+    out = ver.run(inp.W, inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug)
+    torch.cuda.synchronize()
+    res = {}
+    for k, v in out.items():
+        a = v.cpu().numpy()
+        if k == "mask_bits":
+            a = a.view(np.uint32)
+        res[k] = a
+    return res
+
+
+@dataclasses.dataclass
+class Report:
+    decisions: int = 0
+    decision_near_ties: int = 0
+    decision_mismatch_exempt: int = 0
+    argmax_rows: int = 0
+    argmax_near_tie_mismatch: int = 0
+    sequences: int = 0
+    sequence_exempt: int = 0
+    max_logit_err: float = 0.0
+    max_js_err: float = 0.0
+    max_logz_err: float = 0.0
+
+    def add(self, o: "Report"):
+        for f in dataclasses.fields(self):
+            a, b = getattr(self, f.name), getattr(o, f.name)
+            setattr(self, f.name, max(a, b) if f.name.startswith("max_") else a + b)
+
+
+def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
+    """Assert the parity bar; returns the near-tie accounting.  `seqs` are the
+    batch indices the oracle evaluated (its rows, in order)."""
+    modes = np.asarray(modes)
+    n = ora["accept_len"].shape[0]
+    seqs = np.arange(n) if seqs is None else np.asarray(seqs)
+    rep = Report()
+    G = ora["accept_flags"].shape[1]
+    for r, b in enumerate(seqs):
+        mode = int(modes[b])
+        rows = K if mode != wl.LOSSLESS else 1
+        if check_debug:
+            if "mask_bits" in gpu and "mask_bits" in ora:
+                np.testing.assert_array_equal(gpu["mask_bits"][b, :, :rows], ora["mask_bits"][r, :, :rows],
+                                              err_msg=f"mask bits of sequence {b}")
+            if "logits" in gpu and "logits" in ora:
+                err = np.abs(gpu["logits"][b, :, :rows].astype(np.float64) - ora["logits"][r, :, :rows]).max()
+                rep.max_logit_err = max(rep.max_logit_err, float(err))
+                assert err <= LOGIT_TOL, f"logits of sequence {b} off by {err}"
+            lz = np.abs(gpu["head_logz"][b, :, :rows] - ora["head_logz"][r, :, :rows]).max()
+            rep.max_logz_err = max(rep.max_logz_err, float(lz))
+            assert lz <= LOGZ_TOL, f"log-partition of sequence {b} off by {lz}"
+            ga, oa, gap = gpu["head_argmax"][b, :, :rows], ora["head_argmax"][r, :, :rows], ora["head_gap"][r, :, :rows]
+            bad = ga != oa
+            rep.argmax_rows += ga.size
+            assert np.all(gap[bad] < MARGIN), f"head argmax mismatch of sequence {b} at gaps {gap[bad]}"
+            rep.argmax_near_tie_mismatch += int(bad.sum())
+            if rows < K:
+                assert np.all(gpu["head_argmax"][b, :, rows:] == -1)
+            gc, oc, cgap = gpu["centroid_argmax"][b], ora["centroid_argmax"][r], ora["centroid_gap"][r]
+            bad = gc != oc
+            rep.argmax_rows += gc.size
+            assert np.all(cgap[bad] < MARGIN), f"centroid argmax mismatch of sequence {b} at gaps {cgap[bad]}"
+            rep.argmax_near_tie_mismatch += int(bad.sum())
+            if mode == wl.JS and G > 0:
+                e1 = np.abs(gpu["js_heads"][b] - ora["js_heads"][r]).max()
+                e2 = np.abs(gpu["js_draft"][b] - ora["js_draft"][r]).max()
+                rep.max_js_err = max(rep.max_js_err, float(e1), float(e2))
+                assert max(e1, e2) <= JS_TOL, f"JS of sequence {b} off by {max(e1, e2)}"
+        # decisions
+        margin = ora["margin"][r]
+        near = margin < MARGIN
+        rep.decisions += G
+        rep.decision_near_ties += int(near.sum())
+        if "accept_flags" in gpu:
+            gf = gpu["accept_flags"][b].astype(bool)
+            of = ora["accept_flags"][r].astype(bool)
+            bad = gf != of
+            assert np.all(near[bad]), f"decision mismatch of sequence {b} at positions {np.nonzero(bad & ~near)[0]}"
+            rep.decision_mismatch_exempt += int(bad.sum())
+        # accepted length and emitted token
+        A_o = int(ora["accept_len"][r])
+        rep.sequences += 1
+        decisive = near[: min(A_o + 1, G)].any() if G > 0 else False
+        if mode == wl.LOSSLESS:
+            tok_near = ora["race_gap"][r] < RACE_GAP
+        else:
+            tok_near = ora["centroid_gap"][r][A_o] < MARGIN
+        if decisive or tok_near:
+            rep.sequence_exempt += 1
+            continue
+        assert int(gpu["accept_len"][b]) == A_o, f"accept_len of sequence {b}: gpu {gpu['accept_len'][b]} oracle {A_o}"
+        assert int(gpu["out_token"][b]) == int(ora["out_token"][r]), (
+            f"out_token of sequence {b}: gpu {gpu['out_token'][b]} oracle {ora['out_token'][r]}")
+    return rep
+
+
+def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True):
+    return oracle.run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=seqs, want_logits=debug,
+                      want_masks=debug and W.shape[1] % 32 == 0)

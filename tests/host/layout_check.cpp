@@ -1,0 +1,127 @@
+// Host-only check of the LM-head row layout (no HIP call is made): includes
+// the library's host source with the kernel launches stubbed out, then for
+// many shapes verifies that every (sequence, position, head) maps to exactly
+// one physical GEMM row inside the workspace, that row_info inverts
+// lossy_row / lossless_row, and that all workspace indices stay in bounds.
+#include "../../speculative_decoding_verification_philox_amd/csrc/dm_verify.cpp"
+
+#include <cstdio>
+#include <vector>
+
+namespace dmv {
+hipError_t launch_prep(const Plan&, const void*, void*, uint32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_gemm(const Plan&, const void*, const void*, float*, Stat*, hipStream_t) { return hipSuccess; }
+hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*, float*, int32_t*, float*,
+                          hipStream_t) { return hipSuccess; }
+hipError_t launch_js(const Plan&, const float*, const float*, const RowStat*, const RowStat*, float*, hipStream_t) {
+    return hipSuccess;
+}
+hipError_t launch_decide(const Plan&, const int32_t*, const float*, const float*, const RowStat*, const RowStat*,
+                         const float*, int32_t*, int32_t*, unsigned long long*, uint8_t*, float*, float*,
+                         hipStream_t) { return hipSuccess; }
+hipError_t launch_race(const Plan&, const float*, const float*, const RowStat*, const int32_t*, unsigned long long*,
+                       int32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipSuccess; }
+int skinny_strips_per_group() { return 32; }
+}  // namespace dmv
+
+static int fails = 0;
+#define CHECK(c, ...)                                  \
+    do {                                               \
+        if (!(c)) {                                    \
+            if (fails < 20) std::printf(__VA_ARGS__);  \
+            ++fails;                                   \
+        }                                              \
+    } while (0)
+
+static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K, unsigned seed) {
+    dm_verify_desc D{d, V, maxB, gamma, kmax, DM_DTYPE_BF16};
+    std::vector<uint8_t> modes(B);
+    unsigned s = seed;
+    int nl = 0, nj = 0;
+    for (int b = 0; b < B; ++b) {
+        s = s * 1103515245u + 12345u;
+        modes[b] = (uint8_t)((s >> 16) % 3);
+        if (seed == 0) modes[b] = DM_MODE_JS_MAJORITY;
+        if (seed == 1) modes[b] = DM_MODE_LOSSLESS;
+        nl += modes[b] == DM_MODE_LOSSLESS;
+        nj += modes[b] == DM_MODE_JS_MAJORITY;
+    }
+    Plan P{};
+    make_plan(D, B, K, nl, nj, P);
+    for (int b = 0; b < B; ++b) {
+        if (modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
+        if (modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
+    }
+    Sizes sz = workspace_sizes(D);
+    const int T1 = gamma + 1;
+    CHECK((size_t)P.R_phys * d * 2 <= sz.hm, "Hm overflow\n");
+    CHECK((size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) <= sz.part, "part overflow\n");
+    CHECK((size_t)P.n_js_pos * P.js_chunks * (K + 1) * sizeof(float) <= sz.jspart || P.n_js_pos == 0,
+          "jspart overflow\n");
+    CHECK(P.GR * P.ppg <= 64 && P.MT <= 64 && P.ppg >= 1, "tile shape\n");
+    CHECK((long long)P.js_chunks * P.js_chunk >= V && (long long)P.race_chunks * P.race_chunk >= V, "chunks\n");
+    CHECK((P.V + 15) / 16 <= (long long)P.n_vgroups * 32, "vocab groups\n");
+    std::vector<int> seen((size_t)B * T1 * K, 0);
+    for (int rho = 0; rho < P.R_phys; ++rho) {
+        RowInfo ri = row_info(P, rho);
+        if (ri.b < 0) continue;
+        CHECK(ri.b < B && ri.t >= 0 && ri.t < T1 && ri.i >= 0 && ri.i < K, "row %d out of range\n", rho);
+        bool lossless = modes[ri.b] == DM_MODE_LOSSLESS;
+        CHECK(lossless == !ri.lossy, "row %d mode\n", rho);
+        CHECK(!lossless || ri.i == 0, "lossless head\n");
+        seen[((size_t)ri.b * T1 + ri.t) * K + ri.i]++;
+        if (ri.lossy) {
+            CHECK(lossy_row(P, ri.lossy_pos, ri.i) == rho, "lossy_row inverse %d\n", rho);
+            int rank = rank_of(P.lossless_bits, ri.b, false);
+            CHECK(ri.lossy_pos == rank * T1 + ri.t, "lossy position numbering\n");
+        } else {
+            int q = rank_of(P.lossless_bits, ri.b, true) * T1 + ri.t;
+            CHECK(lossless_row(P, q) == rho, "lossless_row inverse %d\n", rho);
+        }
+    }
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < T1; ++t)
+            for (int i = 0; i < K; ++i) {
+                int want = (modes[b] != DM_MODE_LOSSLESS || i == 0) ? 1 : 0;
+                CHECK(seen[((size_t)b * T1 + t) * K + i] == want, "coverage b=%d t=%d i=%d -> %d\n", b, t, i,
+                      seen[((size_t)b * T1 + t) * K + i]);
+            }
+    // a lossy position's heads share one lane group of one tile
+    for (int p = 0; p < P.n_lossy_pos; ++p) {
+        int r0 = lossy_row(P, p, 0);
+        for (int i = 1; i < K; ++i) {
+            int r = lossy_row(P, p, i);
+            int g0, l0, g1, l1;
+            tile_slot(P.geom, r0 % P.MT, &g0, &l0);
+            tile_slot(P.geom, r % P.MT, &g1, &l1);
+            CHECK(r / P.MT == r0 / P.MT && g0 == g1 && l1 == l0 + i, "position %d heads split\n", p);
+        }
+    }
+    // JS positions map to JS sequences
+    for (int jp = 0; jp < P.n_js_pos; ++jp) {
+        int b = select_of(P.js_bits, B, jp / P.G, true);
+        CHECK(b >= 0 && modes[b] == DM_MODE_JS_MAJORITY, "js select\n");
+        CHECK(rank_of(P.js_bits, b, true) == jp / P.G, "js rank\n");
+    }
+}
+
+int main() {
+    int cases = 0;
+    const int Ks[] = {1, 2, 3, 4, 5, 7, 8, 13, 16};
+    for (int kmax : {5, 8, 16})
+        for (int K : Ks) {
+            if (K > kmax) continue;
+            for (int B : {1, 2, 7, 32, 64, 200, 256})
+                for (int gamma : {0, 4, 7, 31})
+                    for (unsigned seed : {0u, 1u, 2u, 3u}) {
+                        check_case(512, 5003, 256, gamma, kmax, B, K, seed);
+                        ++cases;
+                    }
+        }
+    check_case(8192, 128256, 32, 7, 5, 32, 5, 0);
+    check_case(5120, 151936, 64, 5, 8, 64, 8, 2);
+    check_case(4096, 128256, 1, 7, 5, 1, 5, 0);
+    std::printf("%d cases, %d failures\n", cases + 3, fails);
+    return fails ? 1 : 0;
+}

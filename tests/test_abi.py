@@ -1,0 +1,158 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/dm_verify.h declares, and rejects bad arguments on the host before
+any HIP call (dm_verify_check, dm_verify_create on an invalid desc,
+dm_verify_run on a NULL handle)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from speculative_decoding_verification_philox_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dm_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from speculative_decoding_verification_philox_amd import build
+
+        build.build()
+    return B.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dm_verify_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dm_verify_create", "dm_verify_run", "dm_verify_destroy"):
+        assert required in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\b[TW]\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layouts_match_header(lib):
+    # sizes follow from the field lists in include/dm_verify.h on LP64
+    assert ctypes.sizeof(B.dm_verify_desc) == 24
+    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 2 * 8 + 9 * 8
+    assert B.dm_verify_args.seed.offset == 56
+
+
+def desc(**kw):
+    base = dict(d=256, vocab=1000, max_batch=8, gamma=4, k_max=8, dtype=B.DM_DTYPE_BF16)
+    base.update(kw)
+    return B.dm_verify_desc(**base)
+
+
+def args(B_=2, K=5, modes=(B.DM_MODE_JS_MAJORITY, B.DM_MODE_NAIVE), **kw):
+    modes_np = np.asarray(modes if modes is not None else (1, 1), dtype=np.uint8)
+    a = B.dm_verify_args()
+    fake = 0x10000  # never dereferenced: dm_verify_check does not touch memory
+    a.W = a.h = a.draft = a.q_hat = fake
+    a.modes = modes_np.ctypes.data if modes is not None else None
+    a.batch, a.K, a.p_drop, a.reserved, a.seed = B_, K, 0.2, 0, 7
+    a.accept_len = a.out_token = fake
+    for k, v in kw.items():
+        setattr(a, k, v)
+    a._modes = modes_np
+    return a
+
+
+def test_valid_arguments_pass(lib):
+    assert B.dm_verify_check(desc()) == B.DM_OK
+    assert B.dm_verify_check(desc(), args()) == B.DM_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d", 0, B.DM_ERR_INVALID_ARGUMENT),
+    ("d", 96, B.DM_ERR_UNSUPPORTED),
+    ("d", 131072, B.DM_ERR_UNSUPPORTED),
+    ("vocab", 0, B.DM_ERR_INVALID_ARGUMENT),
+    ("vocab", (1 << 24) + 1, B.DM_ERR_INVALID_ARGUMENT),
+    ("max_batch", 0, B.DM_ERR_INVALID_ARGUMENT),
+    ("max_batch", 257, B.DM_ERR_INVALID_ARGUMENT),
+    ("gamma", -1, B.DM_ERR_INVALID_ARGUMENT),
+    ("gamma", 32, B.DM_ERR_INVALID_ARGUMENT),
+    ("k_max", 0, B.DM_ERR_INVALID_ARGUMENT),
+    ("k_max", 17, B.DM_ERR_INVALID_ARGUMENT),
+    ("dtype", 7, B.DM_ERR_UNSUPPORTED),
+])
+def test_bad_desc(lib, field, value, status):
+    assert B.dm_verify_check(desc(**{field: value})) == status
+    assert B.dm_verify_workspace_bytes(desc(**{field: value})) == 0
+    h = ctypes.c_void_p()
+    assert lib.dm_verify_create(ctypes.byref(desc(**{field: value})), ctypes.byref(h)) == status
+    assert not h.value
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(batch=0), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(batch=9), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(K=0), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(K=9), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(p_drop=1.0), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(p_drop=-0.1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(p_drop=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(W=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(h=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(draft=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(modes=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(accept_len=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(out_token=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(q_hat=None), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(W=0x10008), B.DM_ERR_UNSUPPORTED),
+    (dict(h=0x10004), B.DM_ERR_UNSUPPORTED),
+    (dict(q_hat=0x10002), B.DM_ERR_UNSUPPORTED),
+])
+def test_bad_args(lib, change, status):
+    assert B.dm_verify_check(desc(), args(**change)) == status
+
+
+def test_mode_out_of_range(lib):
+    assert B.dm_verify_check(desc(), args(modes=(2, 3))) == B.DM_ERR_INVALID_ARGUMENT
+
+
+def test_naive_needs_no_draft_distribution(lib):
+    assert B.dm_verify_check(desc(), args(modes=(1, 1), q_hat=None)) == B.DM_OK
+    assert B.dm_verify_check(desc(), args(modes=(1, 0), q_hat=None)) == B.DM_ERR_INVALID_ARGUMENT
+
+
+def test_gamma_zero_needs_no_drafts(lib):
+    assert B.dm_verify_check(desc(gamma=0), args(draft=None, q_hat=None)) == B.DM_OK
+
+
+def test_null_handles(lib):
+    assert lib.dm_verify_destroy(None) == B.DM_OK
+    assert lib.dm_verify_profile(None, None, None) == B.DM_ERR_INVALID_ARGUMENT
+    assert lib.dm_verify_run(None, ctypes.byref(args()), None) == B.DM_ERR_INVALID_ARGUMENT
+    assert lib.dm_verify_create(ctypes.byref(desc()), None) == B.DM_ERR_INVALID_ARGUMENT
+    assert lib.dm_verify_create(None, ctypes.byref(ctypes.c_void_p())) == B.DM_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_grows_with_limits(lib):
+    small = B.dm_verify_workspace_bytes(desc())
+    big = B.dm_verify_workspace_bytes(desc(max_batch=64, vocab=151936, d=5120, gamma=5, k_max=8))
+    assert 0 < small < big
+    # the stored logits alone: max_batch * (gamma+1) * k_max * vocab floats
+    assert big >= 64 * 6 * 8 * 151936 * 4
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert B.dm_verify_status_string(s) not in ("", "unknown status")
+    assert B.dm_verify_status_string(99) == "unknown status"

@@ -1,0 +1,145 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  See tests/_parity.py for the bar."""
+import numpy as np
+import pytest
+
+from speculative_decoding_verification_philox_amd import workloads as wl
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not P.gpu_available():
+        pytest.skip("no GPU")
+
+
+def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None):
+    ver = P.make_verifier(W, h, K, max_batch)
+    inp = P.Inputs(W, h, draft, q)
+    rep = P.Report()
+    for seed in seeds:
+        print(f"  seed={seed} B={h.shape[0]} K={K} p={p} modes={np.bincount(modes, minlength=3)}", flush=True)
+        g = P.run_gpu(ver, inp, modes, K, p, seed)
+        o = P.oracle_run(W, h, draft, q, modes, K, p, seed)
+        rep.add(P.compare(g, o, modes, K))
+    ver.close()
+    print(rep, flush=True)
+    if report is not None:
+        report.add(rep)
+    return rep
+
+
+# ------------------------------------------------------------- tiny config
+@pytest.mark.parametrize("mode", [wl.LOSSLESS, wl.NAIVE, wl.JS], ids=["lossless", "naive", "js"])
+def test_tiny_config_each_mode(mode):
+    w = wl.generate(0)
+    modes = np.full(w.cfg.B, mode, np.uint8)
+    rep = _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 21))
+    assert rep.decision_near_ties <= max(1, rep.decisions // 1000)
+
+
+def test_tiny_shapes_batched_mixed_modes():
+    """Config-0 shapes with 24 sequences of mixed rules: several GEMM tiles."""
+    w = wl.generate(0, B=24)
+    modes = np.random.default_rng(3).integers(0, 3, 24).astype(np.uint8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 4))
+
+
+# ------------------------------------------------- bf16, ragged vocabulary
+@pytest.mark.parametrize("K", [1, 3, 5, 8])
+def test_bf16_ragged_vocab_mixed(K):
+    """bf16 inputs, |V| not a multiple of 16, several tiles, all three rules."""
+    w = wl.generate(2, B=12, gamma=5, d=512, V=5003, K=K, planted=0.7)
+    modes = np.array([0, 1, 2] * 4, np.uint8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.25, range(1, 4))
+
+
+def test_bf16_lossless_only_and_naive_only():
+    w = wl.generate(1, B=9, gamma=3, d=256, V=3001, K=4, planted=0.9)
+    for m in (wl.LOSSLESS, wl.NAIVE):
+        _check(w.W, w.h, w.draft, w.q_hat, np.full(9, m, np.uint8), 4, 0.3, range(5, 8))
+
+
+# ----------------------------------------------------------- edge cases
+def test_greedy_reduction_k1_no_dropout():
+    """K = 1, p_drop = 0: the lossy rules are exact match against argmax(W h)."""
+    w = wl.generate(2, B=16, gamma=4, d=256, V=2000, K=1, planted=0.5)
+    target = (wl.as_f32(w.h).astype(np.float64) @ wl.as_f32(w.W).astype(np.float64).T).argmax(-1)
+    draft = np.where(np.random.default_rng(0).random(w.draft.shape) < 0.7, target[:, :-1], w.draft).astype(np.int32)
+    for mode in (wl.NAIVE, wl.JS):
+        modes = np.full(16, mode, np.uint8)
+        ver = P.make_verifier(w.W, w.h, 1)
+        g = P.run_gpu(ver, P.Inputs(w.W, w.h, draft, w.q_hat), modes, 1, 0.0, 9)
+        match = draft == target[:, :-1]
+        np.testing.assert_array_equal(g["accept_flags"].astype(bool), match)
+        A = np.where(match.all(1), match.shape[1], np.argmin(match, axis=1))
+        np.testing.assert_array_equal(g["accept_len"], A)
+        np.testing.assert_array_equal(g["out_token"], target[np.arange(16), A])
+        ver.close()
+
+
+def test_gamma_zero():
+    w = wl.generate(0, B=4, gamma=0)
+    _check(w.W, w.h, w.draft, w.q_hat, np.array([0, 1, 2, 0], np.uint8), 5, 0.2, [3])
+
+
+def test_invalid_drafts_and_zero_q():
+    w = wl.generate(0, B=6, gamma=4)
+    draft = w.draft.copy()
+    draft[0, 0] = -5
+    draft[1, 2] = w.cfg.V
+    q = w.q_hat.copy()
+    q[2, :, :] = 0.0
+    q[2, :, draft[2]] = 0.0
+    q[3, 1, draft[3, 1]] = 0.0  # q(x) = 0: kept iff p(x) > 0
+    modes = np.array([0, 2, 0, 0, 1, 2], np.uint8)
+    _check(w.W, w.h, draft, q, modes, 5, 0.2, [1, 2])
+
+
+def test_determinism_same_seed_same_outputs():
+    import torch
+
+    w = wl.generate(2, B=8, gamma=5, d=512, V=4096, K=5)
+    modes = np.array([0, 1, 2, 2, 1, 0, 2, 2], np.uint8)
+    ver = P.make_verifier(w.W, w.h, 5)
+    inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
+    a = P.run_gpu(ver, inp, modes, 5, 0.2, 77)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = ver.run(inp.W, inp.h, inp.draft, inp.q_hat, modes, 5, 0.2, 77, debug=True)
+    torch.cuda.synchronize()
+    for k in a:
+        np.testing.assert_array_equal(a[k], out[k].cpu().numpy().view(a[k].dtype), err_msg=k)
+    ver.close()
+
+
+# --------------------------------------------------- distribution on GPU
+def test_output_histogram_small_vocab_gpu():
+    """Lossless with drafts drawn exactly from q: the first committed token
+    follows p (Monte-Carlo over 200 calls of 256 independent sequences)."""
+    from tests._oracle_cases import chi2_pvalue, identity_problem
+
+    rng = np.random.default_rng(17)
+    V = 8
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V) * 0.7)
+    Bsz = 256
+    counts = np.zeros(V, np.int64)
+    ver = None
+    for call in range(200):
+        drafts = rng.choice(V, size=(Bsz, 1), p=q)
+        W, h, d, qh = identity_problem(np.broadcast_to(p, (Bsz, 2, V)), np.broadcast_to(q, (Bsz, 1, V)), drafts)
+        # pad d up to the library's multiple of 64 with zero columns
+        Wp = np.zeros((V, 64), np.float32)
+        Wp[:, :V] = W
+        hp = np.zeros((Bsz, 2, 64), np.float32)
+        hp[:, :, :V] = h
+        if ver is None:
+            ver = P.make_verifier(Wp, hp, 1)
+        g = P.run_gpu(ver, P.Inputs(Wp, hp, d, qh), np.zeros(Bsz, np.uint8), 1, 0.0, 1000 + call, debug=False)
+        first = np.where(g["accept_len"] >= 1, drafts[:, 0], g["out_token"])
+        counts += np.bincount(first, minlength=V)
+    ver.close()
+    assert chi2_pvalue(counts, p) > 1e-3
