@@ -30,6 +30,42 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_philox_amd", "csrc", "dm_kernels.hip")
 
 
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded in the process
+    (torch's events are created lazily, so their handles are not usable
+    before torch itself records them)."""
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self) -> int:
+        ev = self.ct.c_void_p()
+        rc = self.lib.hipEventCreate(self.ct.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.made.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.made:
+            self.lib.hipEventDestroy(ev)
+        self.made = []
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -131,20 +167,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    gemm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    hev = HipEvents()
+    gemm_ev = [(hev.create(), hev.create()) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     t_wall = time.perf_counter()
     for i in range(args.steps):
-        Bd.dm_verify_profile(ver.handle, gemm_ev[i][0].cuda_event, gemm_ev[i][1].cuda_event)
+        Bd.dm_verify_profile(ver.handle, gemm_ev[i][0], gemm_ev[i][1])
         step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(stop) / args.steps
-    gemm_ms = [a.elapsed_time(b) for a, b in gemm_ev]
+    gemm_ms = [hev.elapsed_ms(a, b) for a, b in gemm_ev]
+    hev.close()
     gemm_avg = float(np.mean(gemm_ms))
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), wall {wall / args.steps * 1e6:.1f} us/step; "
         f"GEMM kernel {gemm_avg * 1e3:.1f} us avg, min {min(gemm_ms) * 1e3:.1f} us")

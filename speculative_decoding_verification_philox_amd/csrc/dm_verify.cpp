@@ -26,6 +26,7 @@ struct dm_verify {
     RowStat* centstat;
     float* jspart;
     unsigned long long* race;
+    size_t cap_hm, cap_part, cap_jspart;
     hipEvent_t prof_start, prof_stop;
 };
 
@@ -249,6 +250,9 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
     h->centstat = (RowStat*)take(s.centstat);
     h->jspart = (float*)take(s.jspart);
     h->race = (unsigned long long*)take(s.race);
+    h->cap_hm = s.hm;
+    h->cap_part = s.part;
+    h->cap_jspart = s.jspart;
     *out = h;
     return DM_OK;
 }
@@ -291,6 +295,12 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     P.key0 = (uint32_t)(a->seed & 0xffffffffu);
     P.key1 = (uint32_t)(a->seed >> 32);
     P.store_all = a->logits != nullptr;
+    // The workspace was sized for the worst plan of the desc; refuse a plan
+    // that would not fit rather than launch past the end of a buffer.
+    if ((size_t)P.R_phys * D.d * elem_size(D.dtype) > h->cap_hm ||
+        (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) > h->cap_part ||
+        (size_t)P.n_js_pos * P.js_chunks * (P.K + 1) * sizeof(float) > h->cap_jspart)
+        return DM_ERR_UNSUPPORTED;
     float* logits = a->logits ? a->logits : h->logits;
 
     int dev = -1;
