@@ -73,6 +73,12 @@ typedef enum dm_status {
 
 typedef enum dm_dtype { DM_DTYPE_F32 = 0, DM_DTYPE_BF16 = 1 } dm_dtype;
 
+/* Storage order of the LM-head weight W passed to dm_verify_run. */
+typedef enum dm_w_layout {
+    DM_W_ROW_MAJOR = 0, /* [vocab, d] row-major */
+    DM_W_PANELS = 1     /* the panel order written by dm_verify_pack_w (below) */
+} dm_w_layout;
+
 typedef enum dm_mode {
     DM_MODE_LOSSLESS = 0,    /* classical min(1, p/q) test, (p - q)+ residual */
     DM_MODE_NAIVE = 1,       /* DropMatch naive token matching, Eq. (4) */
@@ -91,7 +97,7 @@ typedef struct dm_verify_desc {
 
 /* One verify step.  Shapes use the desc's d, vocab, gamma and this B, K. */
 typedef struct dm_verify_args {
-    const void* W;          /* device [vocab, d] row-major, dtype; 16-byte aligned */
+    const void* W;          /* device LM-head weight, dtype, stored as w_layout says; 16-byte aligned */
     const void* h;          /* device [B, gamma+1, d] row-major, dtype; 16-byte aligned */
     const int32_t* draft;   /* device [B, gamma] drafted token ids (may be NULL iff gamma == 0) */
     const float* q_hat;     /* device [B, gamma, vocab] draft distributions, used as given;
@@ -100,7 +106,7 @@ typedef struct dm_verify_args {
     int32_t batch;          /* B, 1..max_batch */
     int32_t K;              /* dropout heads for lossy sequences, 1..k_max */
     float p_drop;           /* dropout probability, 0 <= p_drop < 1 */
-    uint32_t reserved;      /* must be 0 */
+    uint32_t w_layout;      /* dm_w_layout of W */
     uint64_t seed;          /* Philox key */
     int32_t* accept_len;    /* device out [B]: A, drafts accepted before the first rejection */
     int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
@@ -143,6 +149,25 @@ int dm_verify_check(const dm_verify_desc* desc, const dm_verify_args* args);
 
 /* Device bytes the workspace of `desc` occupies (0 when desc is invalid). */
 size_t dm_verify_workspace_bytes(const dm_verify_desc* desc);
+
+/* Panel order of W (DM_W_PANELS).  The LM head is a fixed weight, so it can
+ * be reordered once, when the model is loaded, into the order in which the
+ * LM-head kernel streams it: each wave then reads one contiguous run of
+ * memory in 1 KiB pieces that are already in matrix-core operand order.
+ *
+ * With E = element size (2 for bf16, 4 for f32), row_bytes = d * E,
+ * nkb = row_bytes / 64 and n_panels = ceil(vocab / 64), the packed buffer
+ * holds n_panels * nkb * 4 * 1024 bytes.  For panel p, fragment kb, strip g
+ * (0..3), lane l (0..63) and byte e (0..15):
+ *   packed[((p * nkb + kb) * 4 + g) * 1024 + l * 16 + e]
+ *     = byte (kb * 64 + (l / 16) * 16 + e) of row (64 p + 16 g + l % 16) of
+ *       row-major W, or 0 when that row is >= vocab.
+ * dm_verify_packed_w_bytes returns the size (0 for an invalid desc).
+ * dm_verify_pack_w enqueues the reordering of row-major device `W` into
+ * device `W_packed` (caller-owned, 16-byte aligned, that many bytes) on
+ * `stream`; it checks its arguments on the host first. */
+size_t dm_verify_packed_w_bytes(const dm_verify_desc* desc);
+int dm_verify_pack_w(const dm_verify_desc* desc, const void* W, void* W_packed, void* stream);
 
 /* Static description of a status code. */
 const char* dm_verify_status_string(int status);

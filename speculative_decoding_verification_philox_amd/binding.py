@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG, "libdmverify.so")
 DM_OK, DM_ERR_INVALID_ARGUMENT, DM_ERR_UNSUPPORTED, DM_ERR_HIP, DM_ERR_OUT_OF_MEMORY = 0, 1, 2, 3, 4
 DM_DTYPE_F32, DM_DTYPE_BF16 = 0, 1
 DM_MODE_LOSSLESS, DM_MODE_NAIVE, DM_MODE_JS_MAJORITY = 0, 1, 2
+DM_W_ROW_MAJOR, DM_W_PANELS = 0, 1
 
 
 class DmError(RuntimeError):
@@ -38,7 +39,7 @@ class dm_verify_args(ctypes.Structure):
     _fields_ = [
         ("W", ctypes.c_void_p), ("h", ctypes.c_void_p), ("draft", ctypes.c_void_p), ("q_hat", ctypes.c_void_p),
         ("modes", ctypes.c_void_p), ("batch", ctypes.c_int32), ("K", ctypes.c_int32), ("p_drop", ctypes.c_float),
-        ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("accept_len", ctypes.c_void_p),
+        ("w_layout", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("accept_len", ctypes.c_void_p),
         ("out_token", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
         ("centroid_argmax", ctypes.c_void_p), ("head_logz", ctypes.c_void_p), ("centroid_logz", ctypes.c_void_p),
         ("js_heads", ctypes.c_void_p), ("js_draft", ctypes.c_void_p), ("logits", ctypes.c_void_p),
@@ -47,7 +48,7 @@ class dm_verify_args(ctypes.Structure):
 
 
 EXPORTS = ("dm_verify_create", "dm_verify_run", "dm_verify_destroy", "dm_verify_profile", "dm_verify_check",
-           "dm_verify_workspace_bytes", "dm_verify_status_string")
+           "dm_verify_workspace_bytes", "dm_verify_status_string", "dm_verify_packed_w_bytes", "dm_verify_pack_w")
 
 _lib = None
 
@@ -71,6 +72,11 @@ def library() -> ctypes.CDLL:
         L.dm_verify_check.restype = ctypes.c_int
         L.dm_verify_workspace_bytes.argtypes = [ctypes.POINTER(dm_verify_desc)]
         L.dm_verify_workspace_bytes.restype = ctypes.c_size_t
+        L.dm_verify_packed_w_bytes.argtypes = [ctypes.POINTER(dm_verify_desc)]
+        L.dm_verify_packed_w_bytes.restype = ctypes.c_size_t
+        L.dm_verify_pack_w.argtypes = [ctypes.POINTER(dm_verify_desc), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        L.dm_verify_pack_w.restype = ctypes.c_int
         L.dm_verify_status_string.argtypes = [ctypes.c_int]
         L.dm_verify_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -88,6 +94,17 @@ def dm_verify_check(desc: dm_verify_desc, args: dm_verify_args | None = None) ->
 
 def dm_verify_workspace_bytes(desc: dm_verify_desc) -> int:
     return int(library().dm_verify_workspace_bytes(ctypes.byref(desc)))
+
+
+def dm_verify_packed_w_bytes(desc: dm_verify_desc) -> int:
+    return int(library().dm_verify_packed_w_bytes(ctypes.byref(desc)))
+
+
+def dm_verify_pack_w(desc: dm_verify_desc, W_ptr: int, W_packed_ptr: int, stream: int | None = None) -> None:
+    rc = library().dm_verify_pack_w(ctypes.byref(desc), ctypes.c_void_p(W_ptr), ctypes.c_void_p(W_packed_ptr),
+                                    ctypes.c_void_p(stream or 0))
+    if rc != DM_OK:
+        raise DmError(rc, "dm_verify_pack_w")
 
 
 def dm_verify_create(desc: dm_verify_desc) -> ctypes.c_void_p:
@@ -143,6 +160,20 @@ class Verifier:
     def workspace_bytes(self) -> int:
         return dm_verify_workspace_bytes(self.desc)
 
+    def pack_w(self, W, stream=None):
+        """Panel-ordered copy of row-major W (a new uint8 device tensor), for
+        runs with w_layout=DM_W_PANELS."""
+        import torch
+
+        D = self.desc
+        elem = torch.bfloat16 if D.dtype == DM_DTYPE_BF16 else torch.float32
+        self._expect("W", W, (D.vocab, D.d), elem, W.device)
+        out = torch.empty(dm_verify_packed_w_bytes(D), dtype=torch.uint8, device=W.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(W.device).cuda_stream
+        dm_verify_pack_w(D, W.data_ptr(), out.data_ptr(), stream)
+        return out
+
     def _expect(self, name, t, shape, dtype, device):
         import torch
 
@@ -158,7 +189,8 @@ class Verifier:
             raise ValueError(f"{name} must be contiguous")
         return t.data_ptr()
 
-    def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, **debug):
+    def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, w_layout=DM_W_ROW_MAJOR,
+                  **debug):
         import torch
 
         D = self.desc
@@ -176,12 +208,18 @@ class Verifier:
         if modes_np.size != B:
             raise ValueError("modes must have one entry per sequence")
         a = dm_verify_args()
-        a.W = self._expect("W", W, (V, d), elem, dev)
+        if w_layout == DM_W_PANELS:
+            a.W = self._expect("W", W, (dm_verify_packed_w_bytes(D),), torch.uint8, dev)
+        elif w_layout == DM_W_ROW_MAJOR:
+            a.W = self._expect("W", W, (V, d), elem, dev)
+        else:
+            raise ValueError(f"unknown w_layout {w_layout}")
+        a.w_layout = int(w_layout)
         a.h = self._expect("h", h, (B, T1, d), elem, dev)
         a.draft = self._expect("draft", draft, (B, G), torch.int32, dev) if G > 0 else None
         a.q_hat = self._expect("q_hat", q_hat, (B, G, V), torch.float32, dev) if q_hat is not None else None
         a.modes = modes_np.ctypes.data
-        a.batch, a.K, a.p_drop, a.reserved = B, int(K), float(p_drop), 0
+        a.batch, a.K, a.p_drop = B, int(K), float(p_drop)
         a.seed = int(seed) & (2**64 - 1)
         a.accept_len = self._expect("accept_len", accept_len, (B,), torch.int32, dev)
         a.out_token = self._expect("out_token", out_token, (B,), torch.int32, dev)
@@ -199,11 +237,14 @@ class Verifier:
         a._keep = (modes_np,)  # keep host memory alive with the struct
         return a
 
-    def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None):
+    def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None,
+            w_layout=DM_W_ROW_MAJOR):
         """Enqueue one verify step on `stream` (default: torch's current stream).
 
-        Returns a dict with accept_len and out_token (and every debug output
-        when debug=True).  Preallocated outputs can be passed in `outputs`."""
+        W is row-major [vocab, d] (w_layout=DM_W_ROW_MAJOR) or the uint8
+        buffer pack_w returns (w_layout=DM_W_PANELS).  Returns a dict with
+        accept_len and out_token (and every debug output when debug=True).
+        Preallocated outputs can be passed in `outputs`."""
         import torch
 
         D = self.desc
@@ -226,7 +267,7 @@ class Verifier:
                 out.setdefault("mask_bits", torch.empty((B, T1, K, D.d // 32), dtype=torch.int32, device=dev))
         dbg = {k: v for k, v in out.items() if k in DEBUG_OUTPUTS}
         args = self.make_args(W, h, draft, q_hat, modes, K, p_drop, seed, out["accept_len"], out["out_token"],
-                              **dbg)
+                              w_layout=w_layout, **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         dm_verify_run(self.handle, args, stream)

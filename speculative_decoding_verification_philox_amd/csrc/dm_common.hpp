@@ -33,6 +33,7 @@ struct Plan {
     int B, T1, G, K, V, d;
     int dtype;           // 0 f32, 1 bf16
     float scale;         // 1 / (1 - p_drop)
+    float inv_k;         // 1 / K, the centroid's mean weight
     uint32_t thresh;     // keep iff Philox word >= thresh
     uint32_t key0, key1; // Philox key (seed low, high)
     // sequences
@@ -46,12 +47,16 @@ struct Plan {
     int tiles_lossy, n_tiles, R_phys;
     // stored logits: rows of [B * T1 * K, V]
     int store_all;
+    // LM-head weight order: 0 row-major, 1 panels of 64 rows (dm_verify_pack_w)
+    int w_packed;
+    int nkb;       // 64-byte fragments per weight row (row bytes / 64)
+    int n_panels;  // ceil(V / 64)
     // vocabulary split of the GEMM's statistic partials
     int n_vgroups;
-    // JS pass
+    // vocabulary pass: JS blocks, then race blocks
     int n_js_pos, js_chunks, js_chunk;
-    // residual race
     int race_chunks, race_chunk;
+    int blk_js, blk_race;
 };
 
 // ------------------------------------------------------------------ layout
@@ -99,6 +104,14 @@ __host__ __device__ inline void tile_slot(int geom, int r, int* g, int* lambda) 
         *lambda = 16 * (r >> 5) + 4 * (rr >> 3) + (rr & 3);
     }
 }
+
+// Per physical GEMM row, written by k_prep for the LM-head epilogue.
+struct RowMeta {
+    int canon;    // (b * T1 + t) * K + i, or -1 for a padding row
+    float scale;  // 1 / (1 - p_drop) for a dropout row, 1 undropped, 0 padding
+    int store;    // 1 if the row's logits are kept for the vocabulary pass
+    int pad;
+};
 
 // What a physical GEMM row holds.
 struct RowInfo {
@@ -214,6 +227,14 @@ __device__ __forceinline__ Stat stat_merge(Stat a, Stat b) {
     return r;
 }
 
+__device__ __forceinline__ Stat stat_shfl_xor(Stat a, int off) {
+    Stat o;
+    o.m = __shfl_xor(a.m, off, 64);
+    o.s = __shfl_xor(a.s, off, 64);
+    o.idx = __shfl_xor(a.idx, off, 64);
+    return o;
+}
+
 // Final per-row statistics.
 struct RowStat {
     float m;
@@ -221,14 +242,14 @@ struct RowStat {
     int idx;
 };
 
-// Mean of the K head logits of one position: the DropMatch centroid logit.
-// Every kernel that forms it goes through this function so the values agree
-// bit for bit.
+// Mean of the K head logits of one position: the DropMatch centroid logit,
+// summed in head order and scaled by inv_k = 1 / K.  Every kernel that forms
+// it uses this order and this scaling, so the values agree bit for bit.
 template <class Get>
-__device__ __forceinline__ float centroid_logit(int K, Get get) {
+__device__ __forceinline__ float centroid_logit(int K, float inv_k, Get get) {
     float s = get(0);
     for (int i = 1; i < K; ++i) s += get(i);
-    return s / (float)K;
+    return s * inv_k;
 }
 
 // ----------------------------------------------------------- bf16 helpers

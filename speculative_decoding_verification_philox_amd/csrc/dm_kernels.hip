@@ -1,14 +1,18 @@
 // dm_kernels.hip -- HIP kernels of the DropMatch verify step for gfx950.
 //
 //   k_prep        dropout masks from Philox, masked hidden rows in GEMM order
-//   k_gemm_skinny LM-head GEMM for short M (all rows of a tile in one
-//                 workgroup; W streamed from HBM straight into MFMA operands),
+//   k_pack_w      one-time reorder of the LM-head weight into panel order
+//   k_gemm_panel  LM-head GEMM over panel-ordered W: one wave streams one
+//                 panel of 64 vocabulary rows straight into MFMA operands,
 //                 with a softmax-statistics epilogue per row and per centroid
+//   k_gemm_skinny LM-head GEMM over row-major W (all rows of a tile in one
+//                 workgroup; W streamed from HBM straight into MFMA operands),
+//                 same epilogue
 //   k_combine     merges the per-vocabulary-group statistics
-//   k_js          Jensen-Shannon terms over the vocabulary
-//   k_decide      acceptance rules, first-reject scan, lossy emit
-//   k_race        exponential race over the residual (lossless emit)
-//   k_emit        picks the race winner
+//   k_vocab       Jensen-Shannon terms and the residual race over the
+//                 vocabulary
+//   k_finish      acceptance rule per drafted position, first-rejection
+//                 scan and the emitted token, one wave per sequence
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,65 +26,255 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // =====================================================================
-// k_prep: Hm[rho, :] = h[b, t, :] * keep(b, t, i, :) for every GEMM row.
+// k_prep: Hm[rho, :] = h[b, t, :] * keep(b, t, i, :) for every GEMM row,
+// plus the row's metadata for the LM-head epilogue.  A thread handles eight
+// elements (two Philox blocks); grid = rows x (d / 2048).
 // DropMatch Sec. 3.1 Eq. (1): independent Bernoulli(1 - p_drop) keeps per
 // (position, head, element), drawn from Philox stream 0 with counter
 // (j / 4, b * (gamma + 1) + t, i, 0).  The inverted-dropout scale of Eq. (2)
 // is applied to the fp32 accumulator later, so masked values stay exact.
-// One block per GEMM row; a thread handles 32 consecutive elements.
+// Hm is written row-major for the row-major-W kernel, or in matrix-core
+// operand order (per tile: [fragment kb][sub-tile m][lane][16 B], lane
+// 16 a + r holding bytes 64 kb + 16 a .. + 16 of sub-tile row r) for the
+// panel kernel.
 // =====================================================================
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restrict__ h, void* __restrict__ Hm,
-                                              uint32_t* __restrict__ dbg_mask) {
+                                              RowMeta* __restrict__ meta, uint32_t* __restrict__ dbg_mask) {
     const int rho = blockIdx.x;
     const RowInfo ri = row_info(P, rho);
-    const int nchunk = P.d >> 5;
-    const int esz = BF16 ? 2 : 4;
-    const size_t src_row = ri.b >= 0 ? (size_t)(ri.b * P.T1 + ri.t) * P.d : 0;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-        uint32_t bits = 0u;
-        if (ri.b >= 0) {
-            if (ri.lossy) {
-                const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
+        RowMeta mt;
+        const bool valid = ri.b >= 0;
+        mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
+        mt.scale = valid ? (ri.lossy ? P.scale : 1.0f) : 0.0f;
+        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
+        mt.pad = 0;
+        meta[rho] = mt;
+    }
+    // this thread: elements 8 e .. 8 e + 7 of the row
+    const int e = blockIdx.y * blockDim.x + threadIdx.x;
+    const int n8 = P.d >> 3;
+    if (e >= n8) return;  // n8 is a multiple of 8: groups of four neighbours leave together
+    constexpr int esz = BF16 ? 2 : 4;
+    constexpr int NV = esz / 2;  // 16-byte pieces per 8 elements
+    uint32_t bits = 0u;          // bit k: keep element 8 e + k
+    if (ri.b >= 0) {
+        if (ri.lossy) {
+            const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    u32x4 r = philox10(u32x4{(uint32_t)(c * 8 + q), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
-                    bits |= (uint32_t)(r.x >= P.thresh) << (4 * q);
-                    bits |= (uint32_t)(r.y >= P.thresh) << (4 * q + 1);
-                    bits |= (uint32_t)(r.z >= P.thresh) << (4 * q + 2);
-                    bits |= (uint32_t)(r.w >= P.thresh) << (4 * q + 3);
-                }
-            } else {
-                bits = 0xffffffffu;
+            for (int q = 0; q < 2; ++q) {
+                const u32x4 rr = philox10(u32x4{(uint32_t)(2 * e + q), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
+                bits |= (uint32_t)(rr.x >= P.thresh) << (4 * q);
+                bits |= (uint32_t)(rr.y >= P.thresh) << (4 * q + 1);
+                bits |= (uint32_t)(rr.z >= P.thresh) << (4 * q + 2);
+                bits |= (uint32_t)(rr.w >= P.thresh) << (4 * q + 3);
             }
+        } else {
+            bits = 0xffu;
         }
-        const uint8_t* src = (const uint8_t*)h + (src_row + (size_t)c * 32) * esz;
-        uint8_t* dst = (uint8_t*)Hm + ((size_t)rho * P.d + (size_t)c * 32) * esz;
+    }
+    const size_t src_row = ri.b >= 0 ? (size_t)(ri.b * P.T1 + ri.t) * P.d : 0;
+    const uint8_t* src = (const uint8_t*)h + (src_row + (size_t)e * 8) * esz;
+    const size_t row_bytes = (size_t)P.d * esz;
+    const int tile = rho / P.MT, r = rho - tile * P.MT;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        v4u x = ri.b >= 0 ? *(const v4u*)(src + 16 * v) : v4u{0, 0, 0, 0};
         if (BF16) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                v4u x = ri.b >= 0 ? *(const v4u*)(src + 16 * v) : v4u{0, 0, 0, 0};
-                uint32_t m8 = (bits >> (8 * v)) & 0xffu;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t w = x[k];
-                    uint32_t lo = (m8 >> (2 * k)) & 1u, hi = (m8 >> (2 * k + 1)) & 1u;
-                    w = (lo ? (w & 0x0000ffffu) : 0u) | (hi ? (w & 0xffff0000u) : 0u);
-                    x[k] = w;
-                }
-                *(v4u*)(dst + 16 * v) = x;
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = (bits >> (2 * k)) & 1u, hi = (bits >> (2 * k + 1)) & 1u;
+                x[k] = (lo ? (x[k] & 0x0000ffffu) : 0u) | (hi ? (x[k] & 0xffff0000u) : 0u);
             }
         } else {
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                v4u x = ri.b >= 0 ? *(const v4u*)(src + 16 * v) : v4u{0, 0, 0, 0};
+            for (int k = 0; k < 4; ++k) x[k] = ((bits >> (4 * v + k)) & 1u) ? x[k] : 0u;
+        }
+        const size_t o = (size_t)e * 8 * esz + 16 * v;  // byte offset within the row
+        size_t dst;
+        if (P.w_packed) {
+            const size_t frag = ((size_t)tile * P.nkb + (o >> 6)) * P.msub + (r >> 4);
+            dst = frag * 1024 + (size_t)(16 * ((o >> 4) & 3) + (r & 15)) * 16;
+        } else {
+            dst = (size_t)rho * row_bytes + o;
+        }
+        *(v4u*)((uint8_t*)Hm + dst) = x;
+    }
+    if (dbg_mask) {
+        // four neighbouring threads hold the 32 bits of one mask word
+        uint32_t word = bits << (8 * (e & 3));
+        word |= __shfl_xor(word, 1, 64);
+        word |= __shfl_xor(word, 2, 64);
+        if (ri.b >= 0 && (e & 3) == 0) dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * (P.d >> 5) + (e >> 2)] = word;
+    }
+}
+
+// =====================================================================
+// k_pack_w: row-major W -> panel order (see dm_verify_pack_w).  One thread
+// per 16-byte piece of the packed buffer.
+// =====================================================================
+__global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ W, uint8_t* __restrict__ Wp, int V,
+                                                int nkb, size_t n16) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= n16) return;
+    const int lane = (int)(q & 63), g = (int)((q >> 6) & 3);
+    const size_t rest = q >> 8;
+    const int kb = (int)(rest % (size_t)nkb);
+    const size_t panel = rest / (size_t)nkb;
+    const size_t row = panel * 64 + (size_t)g * 16 + (lane & 15);
+    const size_t row_bytes = (size_t)nkb * 64;
+    v4u x = v4u{0, 0, 0, 0};
+    if (row < (size_t)V) x = *(const v4u*)(W + row * row_bytes + (size_t)kb * 64 + (lane >> 4) * 16);
+    *(v4u*)(Wp + q * 16) = x;
+}
+
+// =====================================================================
+// k_gemm_panel: L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j]
+// (DropMatch Eq. (3), the shared head W) for one tile of up to 64 rows and
+// one panel of 64 vocabulary rows per wave, W in panel order.
+//
+// Main loop: the wave streams its panel front to back, 1 KiB per load
+// instruction (non-temporal: W is read once), four strips of 16 vocabulary
+// rows per 64-byte fragment; the tile's masked rows come from the packed Hm
+// (L2-resident, shared by every wave).  The next fragment's loads are in
+// flight while the current one feeds v_mfma_f32_16x16x32_bf16 (16x16x4 for
+// fp32).  No LDS and no barrier anywhere in the kernel.
+//
+// Epilogue, straight from the accumulators: lane 16 a + c holds column
+// 16 g + c of rows 16 m + 4 a + j.  Rows later passes need are stored; per
+// row, (max, sum exp, argmax) over the panel's 64 columns comes from the
+// lane's four columns and a butterfly over the 16 lanes of its group.  A
+// position's K head rows sit in one lane group (slot layout), so its
+// centroid (the mean of the heads, DropMatch Eq. (5)) is formed in-lane and
+// reduced the same way.  Results go to part[target][panel].
+// =====================================================================
+constexpr int kPanelWaves = 4;
+constexpr int kPanelStrips = 4;
+constexpr int kPanelNK = 1;  // fragments per pipeline stage
+
+__device__ __forceinline__ Stat stat_reduce16(Stat st) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) x[k] = ((bits >> (4 * v + k)) & 1u) ? x[k] : 0u;
-                *(v4u*)(dst + 16 * v) = x;
+    for (int off = 1; off < 16; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off));
+    return st;
+}
+
+template <bool BF16, int MSUB>
+__global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
+                                                                 const uint8_t* __restrict__ Hp,
+                                                                 const RowMeta* __restrict__ meta,
+                                                                 float* __restrict__ logits,
+                                                                 Stat* __restrict__ part) {
+    constexpr int ROWS = 16 * MSUB, G = kPanelStrips, NK = kPanelNK;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gw = blockIdx.x * kPanelWaves + wave;
+    if (gw >= P.n_panels * P.n_tiles) return;  // nothing below synchronises the block
+    const int panel = gw % P.n_panels, tile = gw / P.n_panels;
+    const int nkb = P.nkb;
+
+    // metadata of tile row `lane`, fetched now, read through shuffles later
+    RowMeta my = RowMeta{-1, 0.0f, 0, 0};
+    if (lane < ROWS) my = meta[(size_t)tile * ROWS + lane];
+
+    v4f acc[G][MSUB];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
+    {
+        const uint8_t* wp = Wp + (size_t)panel * nkb * G * 1024 + lane * 16;
+        const uint8_t* ap = Hp + (size_t)tile * nkb * MSUB * 1024 + lane * 16;
+        v4u wc[NK][G], ac[NK][MSUB], wn[NK][G], an[NK][MSUB];
+        auto load = [&](v4u (&w)[NK][G], v4u (&a)[NK][MSUB], int kb0) {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    w[k][g] = __builtin_nontemporal_load((const v4u*)(wp + ((size_t)(kb0 + k) * G + g) * 1024));
+#pragma unroll
+                for (int m = 0; m < MSUB; ++m) a[k][m] = *(const v4u*)(ap + ((size_t)(kb0 + k) * MSUB + m) * 1024);
+            }
+        };
+        load(wc, ac, 0);
+        for (int kb0 = 0; kb0 < nkb; kb0 += NK) {
+            if (kb0 + NK < nkb) load(wn, an, kb0 + NK);
+#pragma unroll
+            for (int k = 0; k < NK; ++k)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int m = 0; m < MSUB; ++m) {
+                        if (BF16) {
+                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(v8bf, ac[k][m]), __builtin_bit_cast(v8bf, wc[k][g]), acc[g][m], 0,
+                                0, 0);
+                        } else {
+                            const v4f a = __builtin_bit_cast(v4f, ac[k][m]);
+                            const v4f b = __builtin_bit_cast(v4f, wc[k][g]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[g][m], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) wc[k][g] = wn[k][g];
+#pragma unroll
+                for (int m = 0; m < MSUB; ++m) ac[k][m] = an[k][m];
             }
         }
-        if (dbg_mask && ri.b >= 0)
-            dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * nchunk + c] = bits;
+    }
+
+    // ---------------- epilogue ----------------
+    const int grp = lane >> 4, c = lane & 15;
+    const int col0 = panel * 64 + c;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * m + 4 * grp + j;
+            const float sc = __shfl(my.scale, r, 64);
+            const int canon = __shfl(my.canon, r, 64);
+            const int store = __shfl(my.store, r, 64);
+            Stat st = stat_empty();
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float x = acc[g][m][j] * sc;
+                acc[g][m][j] = x;
+                const int col = col0 + 16 * g;
+                if (col < P.V) {
+                    if (store) logits[(size_t)canon * P.V + col] = x;
+                    stat_push(st, x, col);
+                }
+            }
+            st = stat_reduce16(st);
+            if (c == 0) part[(size_t)(tile * ROWS + r) * P.n_panels + panel] = st;
+        }
+    if (tile < P.tiles_lossy) {
+        const int npt = P.GR * P.ppg;
+        for (int slot = 0; slot < P.ppg; ++slot) {
+            const int first = slot * P.K;
+            Stat st = stat_empty();
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                // head rows first .. first + K - 1 of this lane group, summed in head order
+                float sum = 0.0f;
+#pragma unroll
+                for (int lam = 0; lam < 4 * MSUB; ++lam) {
+                    const int i = lam - first;
+                    if (i >= 0 && i < P.K) {
+                        const float v = acc[g][lam >> 2][lam & 3];
+                        sum = i == 0 ? v : sum + v;
+                    }
+                }
+                const int col = col0 + 16 * g;
+                if (col < P.V) stat_push(st, sum * P.inv_k, col);
+            }
+            st = stat_reduce16(st);
+            const int p = tile * npt + grp * P.ppg + slot;
+            if (c == 0 && p < P.n_lossy_pos) part[(size_t)(P.R_phys + p) * P.n_panels + panel] = st;
+        }
     }
 }
 
@@ -298,14 +492,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
         Stat st = stat_empty();
         if (p < P.n_lossy_pos) {
             for (int c = 0; c < ncol; ++c) {
-                float lb = centroid_logit(P.K, [&](int i) { return et[tile_row(0, g, slot * P.K + i) * PITCH + c]; });
+                float lb = centroid_logit(P.K, P.inv_k,
+                                          [&](int i) { return et[tile_row(0, g, slot * P.K + i) * PITCH + c]; });
                 stat_push(st, lb, vbase + c);
             }
         }
         sstat[wave][ROWS + lane] = st;
     }
     __syncthreads();
-    const int n_targets = P.R_phys + P.n_lossy_pos;
     const int nloc = ROWS + (lossy_tile ? npt : 0);
     for (int t = threadIdx.x; t < nloc; t += blockDim.x) {
         Stat st = stat_empty();
@@ -319,26 +513,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
             if (p >= P.n_lossy_pos) continue;
             target = P.R_phys + p;
         }
-        part[(size_t)vg * n_targets + target] = st;
+        part[(size_t)target * P.n_vgroups + vg] = st;
     }
 }
 
 // =====================================================================
 // k_combine: final (max, log Z, argmax) per head row and per centroid.
+// One block per target: threads merge the per-vocabulary-group partials
+// (four loads in flight each), then a butterfly per wave and a fixed-order
+// merge of the waves, so repeated runs give identical bits.
 // =====================================================================
-__global__ __launch_bounds__(256) void k_combine(const Plan P, const Stat* __restrict__ part,
-                                                 RowStat* __restrict__ rowstat, RowStat* __restrict__ centstat,
-                                                 int32_t* __restrict__ dbg_head_arg, float* __restrict__ dbg_head_logz,
-                                                 int32_t* __restrict__ dbg_cent_arg,
-                                                 float* __restrict__ dbg_cent_logz) {
-    const int n_targets = P.R_phys + P.n_lossy_pos;
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n_targets) return;
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const Stat* __restrict__ part,
+                                                             RowStat* __restrict__ rowstat,
+                                                             RowStat* __restrict__ centstat,
+                                                             int32_t* __restrict__ dbg_head_arg,
+                                                             float* __restrict__ dbg_head_logz,
+                                                             int32_t* __restrict__ dbg_cent_arg,
+                                                             float* __restrict__ dbg_cent_logz) {
+    __shared__ Stat s_w[kCombineThreads / 64];
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int b, pos_t, head = 0;
-    bool is_row = t < P.R_phys, lossless = false;
+    const bool is_row = t < P.R_phys;
+    bool lossless = false;
     if (is_row) {
-        RowInfo ri = row_info(P, t);
-        if (ri.b < 0) return;
+        const RowInfo ri = row_info(P, t);
+        if (ri.b < 0) return;  // padding row: the whole block leaves
         b = ri.b;
         pos_t = ri.t;
         head = ri.i;
@@ -348,9 +550,27 @@ __global__ __launch_bounds__(256) void k_combine(const Plan P, const Stat* __res
         b = select_of(P.lossless_bits, P.B, p / P.T1, false);
         pos_t = p % P.T1;
     }
+    const Stat* src = part + (size_t)t * P.n_vgroups;
     Stat st = stat_empty();
-    for (int vg = 0; vg < P.n_vgroups; ++vg) st = stat_merge(st, part[(size_t)vg * n_targets + t]);
-    RowStat rs{st.m, st.m + logf(st.s), st.idx};
+    for (int vg = threadIdx.x; vg < P.n_vgroups; vg += 4 * kCombineThreads) {
+        Stat x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = vg + u * kCombineThreads;
+            x[u] = k < P.n_vgroups ? src[k] : stat_empty();
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) st = stat_merge(st, x[u]);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off));
+    if (lane == 0) s_w[wave] = st;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    st = s_w[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) st = stat_merge(st, s_w[w]);
+    const RowStat rs{st.m, st.m + __logf(st.s), st.idx};
     const int pidx = b * P.T1 + pos_t;
     if (is_row) {
         const int canon = pidx * P.K + head;
@@ -366,236 +586,275 @@ __global__ __launch_bounds__(256) void k_combine(const Plan P, const Stat* __res
 }
 
 // =====================================================================
-// k_js: partial sums over a vocabulary chunk of JS(p^(i) || p-bar) for each
-// head and of JS(q_hat || p-bar) (DropMatch Eq. (6); natural-log divergence
-// with M = (P + Q) / 2).  Each term is evaluated in log space:
-//   log M = max(a, b) + log1p(exp(-|a - b|)) - ln 2,
-//   term  = (e^a (a - log M) + e^b (b - log M)) / 2.
+// k_vocab: the vocabulary pass.
+//
+// Blocks [0, blk_js): one JS position x one vocabulary chunk.  Partial sums
+//   over the chunk of JS(p^(i) || p-bar) for every head i and of
+//   JS(q_hat || p-bar) (DropMatch Eq. (6): natural-log Jensen-Shannon
+//   divergence, M = (P + Q) / 2, 0 ln 0 = 0).
+// Blocks [blk_js, blk_js + blk_race): one lossless sequence x one chunk.
+//   Each block first repeats the sequence's min(1, p/q) tests to find the
+//   first rejection A, then runs the exponential race over its chunk for
+//   the emitted token (the residual (p_A - q_A)+ after a rejection, p_gamma
+//   when every draft passed; "Why speculative decoding preserves
+//   distributions...", Sec. 2 and the verify round of Sec. 5).  Chunk
+//   winners meet in a 64-bit atomic max per sequence.
 // =====================================================================
-__device__ __forceinline__ float js_term(float a, float b) {
-    const float mx = fmaxf(a, b), dl = fabsf(a - b);
-    const float lm = mx + log1pf(__expf(-dl)) - 0.69314718055994531f;
-    return 0.5f * (__expf(a) * (a - lm) + __expf(b) * (b - lm));
+constexpr int kVocabThreads = 256;
+constexpr int kVocabWaves = kVocabThreads / 64;
+constexpr int kJsPerThread = 4;  // the JS chunk is a multiple of kVocabThreads * kJsPerThread
+constexpr float kLn2 = 0.69314718055994531f;
+
+// One vocabulary entry's share of JS(P || Q): with a = ln P, b = ln Q and
+// ln M = ln(P + Q) - ln 2, it is (P (a - ln M) + Q (b - ln M)) / 2, where a
+// zero probability contributes nothing.
+__device__ __forceinline__ float js_entry(float a, float Pa, float b, float Pb) {
+    const float sum = Pa + Pb;
+    if (!(sum > 0.0f)) return 0.0f;
+    const float lm = __logf(sum) - kLn2;
+    const float ta = Pa > 0.0f ? Pa * (a - lm) : 0.0f;
+    const float tb = Pb > 0.0f ? Pb * (b - lm) : 0.0f;
+    return 0.5f * (ta + tb);
 }
 
-__device__ __forceinline__ float js_term_q(float q, float b) {
-    if (!(q > 0.0f)) return 0.5f * __expf(b) * 0.69314718055994531f;
-    return js_term(__logf(q), b);
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
 }
-
-constexpr int kJsThreads = 256;
-
-__global__ __launch_bounds__(kJsThreads) void k_js(const Plan P, const float* __restrict__ logits,
-                                                   const float* __restrict__ q_hat,
-                                                   const RowStat* __restrict__ rowstat,
-                                                   const RowStat* __restrict__ centstat,
-                                                   float* __restrict__ jspart) {
-    const int jp = blockIdx.x, c = blockIdx.y;
-    const int b = select_of(P.js_bits, P.B, jp / P.G, true);
-    const int t = jp % P.G;
-    const int pidx = b * P.T1 + t;
-    const int K = P.K;
-    float logz[kMaxK];
-#pragma unroll
-    for (int i = 0; i < kMaxK; ++i) {
-        logz[i] = 0.0f;
-        if (i < K) logz[i] = rowstat[pidx * K + i].logz;
-    }
-    const float logz_c = centstat[pidx].logz;
-    float acc[kMaxK + 1];
-#pragma unroll
-    for (int i = 0; i <= kMaxK; ++i) acc[i] = 0.0f;
-    const int v0 = c * P.js_chunk;
-    int v1 = v0 + P.js_chunk;
-    v1 = v1 < P.V ? v1 : P.V;
-    const float* lrow = logits + (size_t)pidx * K * P.V;
-    const float* qrow = q_hat + (size_t)(b * P.G + t) * P.V;
-    for (int v = v0 + threadIdx.x; v < v1; v += kJsThreads) {
-        float l[kMaxK];
-#pragma unroll
-        for (int i = 0; i < kMaxK; ++i) {
-            l[i] = 0.0f;
-            if (i < K) l[i] = lrow[(size_t)i * P.V + v];
-        }
-        // same operations, in the same order, as centroid_logit()
-        float lsum = l[0];
-#pragma unroll
-        for (int i = 1; i < kMaxK; ++i)
-            if (i < K) lsum += l[i];
-        const float lb = lsum / (float)K;
-        const float bb = lb - logz_c;
-#pragma unroll
-        for (int i = 0; i < kMaxK; ++i)
-            if (i < K) acc[i] += js_term(l[i] - logz[i], bb);
-        acc[kMaxK] += js_term_q(qrow[v], bb);
-    }
-    // block reduction, fixed order
-    __shared__ float red[kJsThreads / 64][kMaxK + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i <= kMaxK; ++i) {
-        if (i < K || i == kMaxK) {
-            float x = acc[i];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-            if (lane == 0) red[wave][i] = x;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x <= K) {
-        const int i = threadIdx.x == K ? kMaxK : threadIdx.x;
-        float x = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kJsThreads / 64; ++w) x += red[w][i];
-        jspart[((size_t)jp * P.js_chunks + c) * (K + 1) + threadIdx.x] = x;
-    }
-}
-
-// =====================================================================
-// k_decide: one wave per sequence.  Lane t < gamma decides drafted position
-// t with the sequence's rule; a ballot gives the first rejection A
-// ("Speculative Decoding: Draft, Then Verify", the draft-then-verify loop,
-// step 3).  Lossy sequences emit the centroid argmax at A; lossless ones
-// leave the emit to the residual race and reset its slots here.
-// =====================================================================
-__global__ __launch_bounds__(64) void k_decide(const Plan P, const int32_t* __restrict__ draft,
-                                               const float* __restrict__ q_hat, const float* __restrict__ logits,
-                                               const RowStat* __restrict__ rowstat,
-                                               const RowStat* __restrict__ centstat,
-                                               const float* __restrict__ jspart, int32_t* __restrict__ accept_len,
-                                               int32_t* __restrict__ out_token,
-                                               unsigned long long* __restrict__ race_best,
-                                               uint8_t* __restrict__ dbg_flags, float* __restrict__ dbg_js_heads,
-                                               float* __restrict__ dbg_js_draft) {
-    const int b = blockIdx.x, t = threadIdx.x;
-    const int K = P.K, G = P.G, T1 = P.T1;
-    const bool lossless = bit_of(P.lossless_bits, b);
-    const bool js = bit_of(P.js_bits, b);
-    bool reject = false;
-    if (t < G) {
-        const int32_t x = draft[b * G + t];
-        const bool valid = x >= 0 && x < P.V;
-        const int pidx = b * T1 + t;
-        bool accept = false;
-        if (lossless) {
-            if (valid) {
-                const float lx = logits[(size_t)pidx * K * P.V + x];
-                const float px = __expf(lx - rowstat[pidx * K].logz);
-                const float qx = q_hat[(size_t)(b * G + t) * P.V + x];
-                u32x4 r = philox10(u32x4{0u, (uint32_t)pidx, 0u, kStreamAccept}, P.key0, P.key1);
-                const float u = (float)(r.x >> 8) * 5.9604644775390625e-08f;
-                accept = u * qx < px;
-            }
-        } else {
-            int count = 0;
-            for (int i = 0; i < K; ++i) count += rowstat[pidx * K + i].idx == x;
-            if (js) {
-                const int jp = rank_of(P.js_bits, b, true) * G + t;
-                float jmax = -INFINITY, jq = 0.0f;
-                for (int i = 0; i <= K; ++i) {
-                    float s = 0.0f;
-                    for (int c = 0; c < P.js_chunks; ++c) s += jspart[((size_t)jp * P.js_chunks + c) * (K + 1) + i];
-                    if (i < K) {
-                        jmax = fmaxf(jmax, s);
-                        if (dbg_js_heads) dbg_js_heads[(size_t)(b * G + t) * K + i] = s;
-                    } else {
-                        jq = s;
-                    }
-                }
-                if (dbg_js_draft) dbg_js_draft[b * G + t] = jq;
-                accept = valid && (jq <= jmax || 2 * count > K);
-            } else {
-                accept = valid && count > 0;
-            }
-        }
-        reject = !accept;
-        if (dbg_flags) dbg_flags[b * G + t] = accept ? 1 : 0;
-    }
-    const unsigned long long rej = __ballot(reject);
-    const int A = rej ? __ffsll((long long)rej) - 1 : G;
-    if (t == 0) {
-        accept_len[b] = A;
-        if (!lossless) {
-            out_token[b] = centstat[b * T1 + A].idx;
-        } else {
-            race_best[2 * b] = 0ull;
-            race_best[2 * b + 1] = 0ull;
-        }
-    }
-}
-
-// =====================================================================
-// k_race: exponential race over the emit distribution of a lossless
-// sequence ("Why speculative decoding preserves distributions...", Sec. 5:
-// sample normalize((p_A - q_A)+) after a rejection, p_gamma otherwise).
-// Entry v gets the clock E_v = -ln U_v (Philox stream 2); the winner
-// maximises w_v / E_v, smaller v on ties.  A second race over p_A itself
-// covers the zero-residual fallback.  Winners are packed as
-// (key bits << 32) | (~v) and merged with a 64-bit atomic max.
-// =====================================================================
-constexpr int kRaceThreads = 256;
 
 __device__ __forceinline__ unsigned long long race_pack(float key, int v) {
     return ((unsigned long long)__float_as_uint(key) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)v);
 }
 
-__global__ __launch_bounds__(kRaceThreads) void k_race(const Plan P, const float* __restrict__ q_hat,
-                                                       const float* __restrict__ logits,
-                                                       const RowStat* __restrict__ rowstat,
-                                                       const int32_t* __restrict__ accept_len,
-                                                       unsigned long long* __restrict__ race_best) {
-    const int b = select_of(P.lossless_bits, P.B, blockIdx.x, true);
-    const int A = accept_len[b];
-    const int pidx = b * P.T1 + A;
-    const float logz = rowstat[pidx * P.K].logz;
-    const float* lrow = logits + (size_t)pidx * P.K * P.V;
-    const float* qrow = A < P.G ? q_hat + (size_t)(b * P.G + A) * P.V : nullptr;
+__device__ __forceinline__ unsigned long long u64_max(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+
+// Lossy decision at drafted position t of sequence b.
+__device__ __forceinline__ bool lossy_accept(const Plan& P, int b, int t, const int32_t* draft,
+                                             const RowStat* rowstat, bool js, float jq, float jmax) {
+    const int32_t x = draft[b * P.G + t];
+    if (!(x >= 0 && x < P.V)) return false;
+    const int pidx = b * P.T1 + t;
+    int count = 0;
+    for (int i = 0; i < P.K; ++i) count += rowstat[pidx * P.K + i].idx == x;
+    if (!js) return count > 0;             // DropMatch Eq. (4)
+    return jq <= jmax || 2 * count > P.K;  // Algorithm 1: Eq. (6), else Eq. (7)
+}
+
+// Lossless decision at drafted position t: u_t * q(x) < p(x) with p the
+// undropped target distribution and u_t from Philox stream 1.
+__device__ __forceinline__ bool lossless_accept(const Plan& P, int b, int t, const int32_t* draft,
+                                                const float* q_hat, const float* logits,
+                                                const RowStat* rowstat) {
+    const int32_t x = draft[b * P.G + t];
+    if (!(x >= 0 && x < P.V)) return false;
+    const int pidx = b * P.T1 + t;
+    const float px = __expf(logits[(size_t)pidx * P.K * P.V + x] - rowstat[pidx * P.K].logz);
+    const float qx = q_hat[(size_t)(b * P.G + t) * P.V + x];
+    const u32x4 r = philox10(u32x4{0u, (uint32_t)pidx, 0u, kStreamAccept}, P.key0, P.key1);
+    const float u = (float)(r.x >> 8) * 5.9604644775390625e-08f;  // 2^-24
+    return u * qx < px;
+}
+
+// First rejection of a sequence from a wave's per-lane reject flags.
+__device__ __forceinline__ int first_reject(bool reject, int G) {
+    const unsigned long long rej = __ballot(reject);
+    return rej ? __ffsll((long long)rej) - 1 : G;
+}
+
+__global__ __launch_bounds__(kVocabThreads) void k_vocab(
+    const Plan P, const int32_t* __restrict__ draft, const float* __restrict__ q_hat,
+    const float* __restrict__ logits, const RowStat* __restrict__ rowstat, const RowStat* __restrict__ centstat,
+    float* __restrict__ jspart, unsigned long long* __restrict__ race_best) {
+    __shared__ float s_red[kVocabWaves][kMaxK + 1];
+    __shared__ int s_A;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = P.K, G = P.G, T1 = P.T1, V = P.V;
+    int blk = blockIdx.x;
+
+    if (blk < P.blk_js) {
+        const int jp = blk / P.js_chunks, c = blk - jp * P.js_chunks;
+        const int js_rank = jp / G, t = jp - js_rank * G;
+        const int b = select_of(P.js_bits, P.B, js_rank, true);
+        const int pidx = b * T1 + t;
+        float logz[kMaxK];
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) logz[i] = i < K ? rowstat[pidx * K + i].logz : 0.0f;
+        const float logz_c = centstat[pidx].logz;
+        float acc[kMaxK + 1];
+#pragma unroll
+        for (int i = 0; i <= kMaxK; ++i) acc[i] = 0.0f;
+        const float* lrow = logits + (size_t)pidx * K * V;
+        const float* qrow = q_hat + (size_t)(b * G + t) * V;
+        // kJsPerThread entries per thread, all loads issued before any use
+        const int vb = c * P.js_chunk + threadIdx.x;
+        for (int u0 = 0; u0 < P.js_chunk / kVocabThreads; u0 += kJsPerThread) {
+            float l[kJsPerThread][kMaxK];
+            float q[kJsPerThread];
+#pragma unroll
+            for (int u = 0; u < kJsPerThread; ++u) {
+                const int v = vb + (u0 + u) * kVocabThreads;
+                const bool ok = v < V;
+#pragma unroll
+                for (int i = 0; i < kMaxK; ++i) l[u][i] = (i < K && ok) ? lrow[(size_t)i * V + v] : 0.0f;
+                q[u] = ok ? qrow[v] : -1.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kJsPerThread; ++u) {
+                if (q[u] < 0.0f) continue;  // past the end of the vocabulary
+                // the centroid logit, same operations in the same order as
+                // the LM-head epilogue's centroid_logit()
+                float lsum = l[u][0];
+#pragma unroll
+                for (int i = 1; i < kMaxK; ++i)
+                    if (i < K) lsum += l[u][i];
+                const float bb = lsum * P.inv_k - logz_c;
+                const float pb = __expf(bb);
+#pragma unroll
+                for (int i = 0; i < kMaxK; ++i)
+                    if (i < K) {
+                        const float a = l[u][i] - logz[i];
+                        acc[i] += js_entry(a, __expf(a), bb, pb);
+                    }
+                acc[kMaxK] += q[u] > 0.0f ? js_entry(__logf(q[u]), q[u], bb, pb) : js_entry(0.0f, 0.0f, bb, pb);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i <= kMaxK; ++i)
+            if (i < K || i == kMaxK) {
+                const float x = wave_sum(acc[i]);
+                if (lane == 0) s_red[wave][i] = x;
+            }
+        __syncthreads();
+        if (threadIdx.x <= K) {
+            const int i = threadIdx.x == K ? kMaxK : threadIdx.x;
+            float x = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kVocabWaves; ++w) x += s_red[w][i];
+            jspart[((size_t)jp * (K + 1) + threadIdx.x) * P.js_chunks + c] = x;
+        }
+        return;
+    }
+    blk -= P.blk_js;
+
+    const int r = blk / P.race_chunks, c = blk - r * P.race_chunks;
+    const int b = select_of(P.lossless_bits, P.B, r, true);
+    if (wave == 0) {
+        const bool reject = lane < G && !lossless_accept(P, b, lane, draft, q_hat, logits, rowstat);
+        const int A = first_reject(reject, G);
+        if (lane == 0) s_A = A;
+    }
+    __syncthreads();
+    const int A = s_A;
+    const int pidx = b * T1 + A;
+    const float logz = rowstat[pidx * K].logz;
+    const float* lrow = logits + (size_t)pidx * K * V;
+    const float* qrow = A < G ? q_hat + (size_t)(b * G + A) * V : nullptr;
     unsigned long long best_r = 0ull, best_p = 0ull;
-    const int v0 = blockIdx.y * P.race_chunk;
-    int v1 = v0 + P.race_chunk;
-    v1 = v1 < P.V ? v1 : P.V;
-    for (int vq = v0 + 4 * threadIdx.x; vq < v1; vq += 4 * kRaceThreads) {
-        u32x4 r = philox10(u32x4{(uint32_t)(vq >> 2), (uint32_t)pidx, 0u, kStreamRace}, P.key0, P.key1);
-        const uint32_t words[4] = {r.x, r.y, r.z, r.w};
+    const int v0 = c * P.race_chunk;
+    const int v1 = min(v0 + P.race_chunk, V);
+    for (int vq = v0 + 4 * threadIdx.x; vq < v1; vq += 4 * kVocabThreads) {
+        float lv[4], qv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool ok = vq + k < v1;
+            lv[k] = ok ? lrow[vq + k] : 0.0f;
+            qv[k] = (ok && qrow) ? qrow[vq + k] : 0.0f;
+        }
+        const u32x4 rr = philox10(u32x4{(uint32_t)(vq >> 2), (uint32_t)pidx, 0u, kStreamRace}, P.key0, P.key1);
+        const uint32_t words[4] = {rr.x, rr.y, rr.z, rr.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int v = vq + k;
-            if (v >= v1) break;
-            const float p = __expf(lrow[v] - logz);
-            const float w = qrow ? fmaxf(p - qrow[v], 0.0f) : p;
+            if (v >= v1) continue;
+            const float p = __expf(lv[k] - logz);
+            const float w = qrow ? fmaxf(p - qv[k], 0.0f) : p;
+            // U in (0, 1): top 23 bits plus one half, times 2^-23
             const float U = ((float)(words[k] >> 9) + 0.5f) * 1.1920928955078125e-07f;
-            const float E = -logf(U);
-            if (w > 0.0f) {
-                unsigned long long kr = race_pack(w / E, v);
-                best_r = kr > best_r ? kr : best_r;
-            }
-            if (p > 0.0f) {
-                unsigned long long kp = race_pack(p / E, v);
-                best_p = kp > best_p ? kp : best_p;
-            }
+            const float E = -__logf(U);
+            if (w > 0.0f) best_r = u64_max(best_r, race_pack(w / E, v));
+            if (p > 0.0f) best_p = u64_max(best_p, race_pack(p / E, v));
         }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        unsigned long long o = __shfl_xor(best_r, off, 64);
-        best_r = o > best_r ? o : best_r;
-        o = __shfl_xor(best_p, off, 64);
-        best_p = o > best_p ? o : best_p;
+        best_r = u64_max(best_r, __shfl_xor(best_r, off, 64));
+        best_p = u64_max(best_p, __shfl_xor(best_p, off, 64));
     }
-    if ((threadIdx.x & 63) == 0) {
+    if (lane == 0) {
         if (best_r) atomicMax(&race_best[2 * b], best_r);
         if (best_p) atomicMax(&race_best[2 * b + 1], best_p);
     }
 }
 
-__global__ __launch_bounds__(256) void k_emit(const Plan P, const unsigned long long* __restrict__ race_best,
-                                              int32_t* __restrict__ out_token) {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= P.n_lossless_seq) return;
-    const int b = select_of(P.lossless_bits, P.B, r, true);
-    unsigned long long best = race_best[2 * b];
-    if (!best) best = race_best[2 * b + 1];
-    out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
+// =====================================================================
+// k_finish: one wave per sequence.  Applies the sequence's rule at every
+// drafted position (lane t decides position t), finds the first rejection A
+// ("Speculative Decoding: Draft, Then Verify", the draft-then-verify loop,
+// steps 3 and 4) and emits one token: the centroid argmax at A for the
+// DropMatch rules, the race winner for lossless sequences (whose race slots
+// it then clears for the next call).  JS sums over the vocabulary chunks
+// are reduced here in a fixed order.
+// =====================================================================
+__global__ __launch_bounds__(64) void k_finish(const Plan P, const int32_t* __restrict__ draft,
+                                               const float* __restrict__ q_hat, const float* __restrict__ logits,
+                                               const RowStat* __restrict__ rowstat,
+                                               const RowStat* __restrict__ centstat,
+                                               const float* __restrict__ jspart,
+                                               unsigned long long* __restrict__ race_best,
+                                               int32_t* __restrict__ accept_len, int32_t* __restrict__ out_token,
+                                               uint8_t* __restrict__ dbg_flags, float* __restrict__ dbg_js_heads,
+                                               float* __restrict__ dbg_js_draft) {
+    __shared__ float s_js[32][kMaxK + 1];
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int K = P.K, G = P.G, T1 = P.T1;
+    const bool lossless = bit_of(P.lossless_bits, b);
+    const bool js = bit_of(P.js_bits, b);
+    if (js && G > 0) {
+        // lane `idx` sums one (position, head-or-draft) over the chunks in
+        // chunk order; partials are laid out [JS position][K + 1][chunk]
+        const int jp0 = rank_of(P.js_bits, b, true) * G;
+        for (int idx = lane; idx < G * (K + 1); idx += 64) {
+            const float* src = jspart + ((size_t)jp0 * (K + 1) + idx) * P.js_chunks;
+            float x = 0.0f;
+#pragma unroll 8
+            for (int cc = 0; cc < P.js_chunks; ++cc) x += src[cc];
+            s_js[idx / (K + 1)][idx % (K + 1)] = x;
+        }
+        __syncthreads();
+    }
+    bool accept = false;
+    if (lane < G) {
+        if (lossless) {
+            accept = lossless_accept(P, b, lane, draft, q_hat, logits, rowstat);
+        } else if (js) {
+            float jmax = -INFINITY;
+            for (int i = 0; i < K; ++i) jmax = fmaxf(jmax, s_js[lane][i]);
+            const float jq = s_js[lane][K];
+            accept = lossy_accept(P, b, lane, draft, rowstat, true, jq, jmax);
+            if (dbg_js_draft) dbg_js_draft[b * G + lane] = jq;
+            if (dbg_js_heads)
+                for (int i = 0; i < K; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
+        } else {
+            accept = lossy_accept(P, b, lane, draft, rowstat, false, 0.0f, 0.0f);
+        }
+        if (dbg_flags) dbg_flags[b * G + lane] = accept ? 1 : 0;
+    }
+    const int A = first_reject(lane < G && !accept, G);
+    if (lane == 0) {
+        accept_len[b] = A;
+        if (lossless) {
+            unsigned long long best = race_best[2 * b];
+            if (!best) best = race_best[2 * b + 1];
+            out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
+            race_best[2 * b] = 0ull;
+            race_best[2 * b + 1] = 0ull;
+        } else {
+            out_token[b] = centstat[b * T1 + A].idx;  // greedy on the centroid at A
+        }
+    }
 }
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {
@@ -606,11 +865,35 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {
 // =====================================================================
 // launch wrappers
 // =====================================================================
-hipError_t launch_prep(const Plan& P, const void* h, void* Hm, uint32_t* dbg_mask, hipStream_t st) {
+hipError_t launch_prep(const Plan& P, const void* h, void* Hm, RowMeta* meta, uint32_t* dbg_mask, hipStream_t st) {
+    const dim3 grid(P.R_phys, ((P.d >> 3) + 255) / 256);
     if (P.dtype == 1)
-        hipLaunchKernelGGL(k_prep<true>, dim3(P.R_phys), dim3(256), 0, st, P, h, Hm, dbg_mask);
+        hipLaunchKernelGGL(k_prep<true>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
     else
-        hipLaunchKernelGGL(k_prep<false>, dim3(P.R_phys), dim3(256), 0, st, P, h, Hm, dbg_mask);
+        hipLaunchKernelGGL(k_prep<false>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w(const void* W, void* Wp, int V, int nkb, size_t n16, hipStream_t st) {
+    const size_t blocks = (n16 + 255) / 256;
+    hipLaunchKernelGGL(k_pack_w, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)W, (uint8_t*)Wp, V, nkb,
+                       n16);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_panel_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
+                                 Stat* part, hipStream_t st) {
+    const int work = P.n_panels * P.n_tiles;
+    dim3 grid((work + kPanelWaves - 1) / kPanelWaves), block(kPanelWaves * 64);
+    const uint8_t* w = (const uint8_t*)Wp;
+    const uint8_t* a = (const uint8_t*)Hp;
+    switch (P.msub) {
+        case 1: hipLaunchKernelGGL((k_gemm_panel<BF16, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 2: hipLaunchKernelGGL((k_gemm_panel<BF16, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 3: hipLaunchKernelGGL((k_gemm_panel<BF16, 3>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        default: hipLaunchKernelGGL((k_gemm_panel<BF16, 4>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+    }
     return hipGetLastError();
 }
 
@@ -629,7 +912,11 @@ static hipError_t launch_skinny_t(const Plan& P, const void* W, const void* Hm, 
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const Plan& P, const void* W, const void* Hm, float* logits, Stat* part, hipStream_t st) {
+hipError_t launch_gemm(const Plan& P, const void* W, const void* Hm, const RowMeta* meta, float* logits, Stat* part,
+                       hipStream_t st) {
+    if (P.w_packed)
+        return P.dtype == 1 ? launch_panel_t<true>(P, W, Hm, meta, logits, part, st)
+                            : launch_panel_t<false>(P, W, Hm, meta, logits, part, st);
     return P.dtype == 1 ? launch_skinny_t<true>(P, W, Hm, logits, part, st)
                         : launch_skinny_t<false>(P, W, Hm, logits, part, st);
 }
@@ -639,34 +926,23 @@ int skinny_strips_per_group() { return kSkinnyNS * kSkinnyWaves; }
 hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, RowStat* centstat, int32_t* dbg_head_arg,
                           float* dbg_head_logz, int32_t* dbg_cent_arg, float* dbg_cent_logz, hipStream_t st) {
     const int n = P.R_phys + P.n_lossy_pos;
-    hipLaunchKernelGGL(k_combine, dim3((n + 255) / 256), dim3(256), 0, st, P, part, rowstat, centstat, dbg_head_arg,
+    hipLaunchKernelGGL(k_combine, dim3(n), dim3(kCombineThreads), 0, st, P, part, rowstat, centstat, dbg_head_arg,
                        dbg_head_logz, dbg_cent_arg, dbg_cent_logz);
     return hipGetLastError();
 }
 
-hipError_t launch_js(const Plan& P, const float* logits, const float* q_hat, const RowStat* rowstat,
-                     const RowStat* centstat, float* jspart, hipStream_t st) {
-    hipLaunchKernelGGL(k_js, dim3(P.n_js_pos, P.js_chunks), dim3(kJsThreads), 0, st, P, logits, q_hat, rowstat,
-                       centstat, jspart);
-    return hipGetLastError();
-}
-
-hipError_t launch_decide(const Plan& P, const int32_t* draft, const float* q_hat, const float* logits,
-                         const RowStat* rowstat, const RowStat* centstat, const float* jspart, int32_t* accept_len,
-                         int32_t* out_token, unsigned long long* race_best, uint8_t* dbg_flags, float* dbg_js_heads,
-                         float* dbg_js_draft, hipStream_t st) {
-    hipLaunchKernelGGL(k_decide, dim3(P.B), dim3(64), 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
-                       accept_len, out_token, race_best, dbg_flags, dbg_js_heads, dbg_js_draft);
-    return hipGetLastError();
-}
-
-hipError_t launch_race(const Plan& P, const float* q_hat, const float* logits, const RowStat* rowstat,
-                       const int32_t* accept_len, unsigned long long* race_best, int32_t* out_token, hipStream_t st) {
-    hipLaunchKernelGGL(k_race, dim3(P.n_lossless_seq, P.race_chunks), dim3(kRaceThreads), 0, st, P, q_hat, logits,
-                       rowstat, accept_len, race_best);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_emit, dim3((P.n_lossless_seq + 255) / 256), dim3(256), 0, st, P, race_best, out_token);
+hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const float* logits,
+                        const RowStat* rowstat, const RowStat* centstat, float* jspart,
+                        unsigned long long* race_best, int32_t* accept_len, int32_t* out_token, uint8_t* dbg_flags,
+                        float* dbg_js_heads, float* dbg_js_draft, hipStream_t st) {
+    if (P.blk_js + P.blk_race > 0) {
+        hipLaunchKernelGGL(k_vocab, dim3(P.blk_js + P.blk_race), dim3(kVocabThreads), 0, st, P, draft, q_hat, logits,
+                           rowstat, centstat, jspart, race_best);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(64), 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
+                       race_best, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
 }
 

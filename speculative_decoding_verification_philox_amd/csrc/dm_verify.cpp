@@ -24,9 +24,10 @@ struct dm_verify {
     Stat* part;
     RowStat* rowstat;
     RowStat* centstat;
+    RowMeta* meta;
     float* jspart;
     unsigned long long* race;
-    size_t cap_hm, cap_part, cap_jspart;
+    size_t cap_hm, cap_part, cap_jspart, cap_meta_rows;
     hipEvent_t prof_start, prof_stop;
 };
 
@@ -53,7 +54,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
     if (!a) return DM_ERR_INVALID_ARGUMENT;
-    if (a->reserved != 0) return DM_ERR_INVALID_ARGUMENT;
+    if (a->w_layout != DM_W_ROW_MAJOR && a->w_layout != DM_W_PANELS) return DM_ERR_INVALID_ARGUMENT;
     if (a->batch < 1 || a->batch > D->max_batch) return DM_ERR_INVALID_ARGUMENT;
     if (a->K < 1 || a->K > D->k_max) return DM_ERR_INVALID_ARGUMENT;
     if (!(a->p_drop >= 0.0f && a->p_drop < 1.0f)) return DM_ERR_INVALID_ARGUMENT;
@@ -85,7 +86,8 @@ uint32_t drop_threshold(float p_drop) {
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Row layout and work split of one call.
-void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, Plan& P) {
+void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, int w_packed, Plan& P) {
+    // counts only; the sequence bit sets are filled in by the caller
     P.B = B;
     P.T1 = D.gamma + 1;
     P.G = D.gamma;
@@ -122,23 +124,27 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
     P.n_tiles = best_tiles;
     P.R_phys = P.n_tiles * P.MT;
 
-    const int nstr = cdiv(P.V, 16);
-    const int spg = skinny_strips_per_group();
-    int ng = cdiv(nstr, spg);
-    const int fill = nstr < 256 ? nstr : 256;
-    P.n_vgroups = ng > fill ? ng : fill;
-
-    P.n_js_pos = n_js * P.G;
-    P.js_chunks = 1;
-    P.js_chunk = P.V;
-    if (P.n_js_pos > 0) {
-        int ch = cdiv(2048, P.n_js_pos);
-        const int chmax = cdiv(P.V, 256);
-        ch = ch < 1 ? 1 : (ch > chmax ? chmax : ch);
-        P.js_chunk = cdiv(cdiv(P.V, ch), 256) * 256;
-        P.js_chunks = cdiv(P.V, P.js_chunk);
+    P.w_packed = w_packed;
+    P.nkb = (int)((size_t)D.d * elem_size(D.dtype) / 64);
+    P.n_panels = cdiv(P.V, 64);
+    if (w_packed) {
+        // one wave per (panel, tile); statistic partials per panel
+        P.n_vgroups = P.n_panels;
+    } else {
+        const int nstr = cdiv(P.V, 16);
+        const int spg = skinny_strips_per_group();
+        int ng = cdiv(nstr, spg);
+        const int fill = nstr < 256 ? nstr : 256;
+        P.n_vgroups = ng > fill ? ng : fill;
     }
-    P.race_chunks = 1;
+
+    // vocabulary pass: JS positions split into chunks of 1024 entries (four
+    // per thread of a 256-thread block)
+    P.n_js_pos = n_js * P.G;
+    P.js_chunks = 0;
+    P.js_chunk = 1024;
+    if (P.n_js_pos > 0) P.js_chunks = cdiv(P.V, P.js_chunk);
+    P.race_chunks = 0;
     P.race_chunk = P.V;
     if (n_lossless > 0) {
         int ch = cdiv(1024, n_lossless);
@@ -147,39 +153,41 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         P.race_chunk = cdiv(cdiv(P.V, ch), 1024) * 1024;
         P.race_chunks = cdiv(P.V, P.race_chunk);
     }
+    P.blk_js = P.n_js_pos * P.js_chunks;
+    P.blk_race = n_lossless * P.race_chunks;
 }
 
 struct Sizes {
-    size_t hm, logits, part, rowstat, centstat, jspart, race;
+    size_t hm, logits, part, rowstat, centstat, meta, jspart, race;
 };
 
 Sizes workspace_sizes(const dm_verify_desc& D) {
     Sizes s{};
     const size_t T1 = (size_t)D.gamma + 1;
     size_t max_hm_rows = 0, max_part = 0, max_js = 0;
-    for (int K = 1; K <= D.k_max; ++K) {
-        for (int nl = 0; nl <= D.max_batch; ++nl) {
-            Plan P{};
-            make_plan(D, D.max_batch, K, nl, D.max_batch - nl, P);
-            if ((size_t)P.R_phys > max_hm_rows) max_hm_rows = P.R_phys;
-            size_t part = (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos);
-            if (part > max_part) max_part = part;
-            // JS positions can be any count up to max_batch * gamma
+    for (int wp = 0; wp <= 1; ++wp)
+        for (int K = 1; K <= D.k_max; ++K) {
+            for (int nl = 0; nl <= D.max_batch; ++nl) {
+                Plan P{};
+                make_plan(D, D.max_batch, K, nl, D.max_batch - nl, wp, P);
+                if ((size_t)P.R_phys > max_hm_rows) max_hm_rows = P.R_phys;
+                size_t part = (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos);
+                if (part > max_part) max_part = part;
+            }
         }
-    }
+    // JS positions can be any count up to max_batch * gamma
     for (int nj = 1; nj <= D.max_batch; ++nj) {
-        for (int K = D.k_max; K <= D.k_max; ++K) {
-            Plan P{};
-            make_plan(D, D.max_batch, K, 0, nj, P);
-            size_t js = (size_t)P.n_js_pos * P.js_chunks * (K + 1);
-            if (js > max_js) max_js = js;
-        }
+        Plan P{};
+        make_plan(D, D.max_batch, D.k_max, 0, nj, 0, P);
+        size_t js = (size_t)P.n_js_pos * P.js_chunks * (D.k_max + 1);
+        if (js > max_js) max_js = js;
     }
     s.hm = max_hm_rows * (size_t)D.d * elem_size(D.dtype);
     s.logits = (size_t)D.max_batch * T1 * D.k_max * D.vocab * sizeof(float);
     s.part = max_part * sizeof(Stat);
     s.rowstat = (size_t)D.max_batch * T1 * D.k_max * sizeof(RowStat);
     s.centstat = (size_t)D.max_batch * T1 * sizeof(RowStat);
+    s.meta = max_hm_rows * sizeof(RowMeta);
     s.jspart = (max_js > 0 ? max_js : 1) * sizeof(float);
     s.race = (size_t)D.max_batch * 2 * sizeof(unsigned long long);
     return s;
@@ -188,7 +196,7 @@ Sizes workspace_sizes(const dm_verify_desc& D) {
 size_t total_bytes(const Sizes& s) {
     const size_t a = 256;
     return align_up(s.hm, a) + align_up(s.logits, a) + align_up(s.part, a) + align_up(s.rowstat, a) +
-           align_up(s.centstat, a) + align_up(s.jspart, a) + align_up(s.race, a);
+           align_up(s.centstat, a) + align_up(s.meta, a) + align_up(s.jspart, a) + align_up(s.race, a);
 }
 
 }  // namespace
@@ -248,12 +256,40 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
     h->part = (Stat*)take(s.part);
     h->rowstat = (RowStat*)take(s.rowstat);
     h->centstat = (RowStat*)take(s.centstat);
+    h->meta = (RowMeta*)take(s.meta);
     h->jspart = (float*)take(s.jspart);
     h->race = (unsigned long long*)take(s.race);
+    // The race winners start at zero; the kernel that consumes them clears
+    // them at the end of every call.
+    e = hipMemset(h->race, 0, s.race);
+    if (e != hipSuccess) {
+        (void)hipFree(h->ws);
+        delete h;
+        (void)hipGetLastError();
+        return DM_ERR_HIP;
+    }
     h->cap_hm = s.hm;
+    h->cap_meta_rows = s.meta / sizeof(RowMeta);
     h->cap_part = s.part;
     h->cap_jspart = s.jspart;
     *out = h;
+    return DM_OK;
+}
+
+size_t dm_verify_packed_w_bytes(const dm_verify_desc* desc) {
+    if (check_desc(desc) != DM_OK) return 0;
+    const size_t nkb = (size_t)desc->d * elem_size(desc->dtype) / 64;
+    return (size_t)cdiv(desc->vocab, 64) * nkb * 4 * 1024;
+}
+
+int dm_verify_pack_w(const dm_verify_desc* desc, const void* W, void* W_packed, void* stream) {
+    int rc = check_desc(desc);
+    if (rc != DM_OK) return rc;
+    if (!W || !W_packed) return DM_ERR_INVALID_ARGUMENT;
+    if (!aligned(W, 16) || !aligned(W_packed, 16)) return DM_ERR_UNSUPPORTED;
+    const int nkb = (int)((size_t)desc->d * elem_size(desc->dtype) / 64);
+    const size_t n16 = dm_verify_packed_w_bytes(desc) / 16;
+    if (launch_pack_w(W, W_packed, desc->vocab, nkb, n16, (hipStream_t)stream) != hipSuccess) return DM_ERR_HIP;
     return DM_OK;
 }
 
@@ -285,19 +321,20 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
         n_lossless += a->modes[b] == DM_MODE_LOSSLESS;
         n_js += a->modes[b] == DM_MODE_JS_MAJORITY;
     }
-    make_plan(D, a->batch, a->K, n_lossless, n_js, P);
+    make_plan(D, a->batch, a->K, n_lossless, n_js, (int)a->w_layout, P);
     for (int b = 0; b < a->batch; ++b) {
         if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
     }
     P.scale = (float)(1.0 / (1.0 - (double)a->p_drop));
+    P.inv_k = 1.0f / (float)a->K;
     P.thresh = drop_threshold(a->p_drop);
     P.key0 = (uint32_t)(a->seed & 0xffffffffu);
     P.key1 = (uint32_t)(a->seed >> 32);
     P.store_all = a->logits != nullptr;
     // The workspace was sized for the worst plan of the desc; refuse a plan
     // that would not fit rather than launch past the end of a buffer.
-    if ((size_t)P.R_phys * D.d * elem_size(D.dtype) > h->cap_hm ||
+    if ((size_t)P.R_phys * D.d * elem_size(D.dtype) > h->cap_hm || (size_t)P.R_phys > h->cap_meta_rows ||
         (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) > h->cap_part ||
         (size_t)P.n_js_pos * P.js_chunks * (P.K + 1) * sizeof(float) > h->cap_jspart)
         return DM_ERR_UNSUPPORTED;
@@ -315,21 +352,18 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     } while (0)
     if (a->head_argmax) DM_TRY(launch_fill_i32(a->head_argmax, a->batch * T1 * a->K, -1, st));
     if (a->mask_bits) DM_TRY(launch_fill_i32((int32_t*)a->mask_bits, a->batch * T1 * a->K * (D.d / 32), 0, st));
-    DM_TRY(launch_prep(P, a->h, h->Hm, a->mask_bits, st));
+    DM_TRY(launch_prep(P, a->h, h->Hm, h->meta, a->mask_bits, st));
     const bool prof = h->prof_start && h->prof_stop;
     if (prof) DM_TRY(hipEventRecord(h->prof_start, st));
-    DM_TRY(launch_gemm(P, a->W, h->Hm, logits, h->part, st));
+    DM_TRY(launch_gemm(P, a->W, h->Hm, h->meta, logits, h->part, st));
     if (prof) {
         DM_TRY(hipEventRecord(h->prof_stop, st));
         h->prof_start = h->prof_stop = nullptr;
     }
     DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, a->head_argmax, a->head_logz, a->centroid_argmax,
                           a->centroid_logz, st));
-    if (P.n_js_pos > 0) DM_TRY(launch_js(P, logits, a->q_hat, h->rowstat, h->centstat, h->jspart, st));
-    DM_TRY(launch_decide(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, a->accept_len,
-                         a->out_token, h->race, a->accept_flags, a->js_heads, a->js_draft, st));
-    if (P.n_lossless_seq > 0)
-        DM_TRY(launch_race(P, a->q_hat, logits, h->rowstat, a->accept_len, h->race, a->out_token, st));
+    DM_TRY(launch_vocab(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, h->race, a->accept_len,
+                        a->out_token, a->accept_flags, a->js_heads, a->js_draft, st));
 #undef DM_TRY
     return DM_OK;
 }

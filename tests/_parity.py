@@ -44,10 +44,31 @@ def to_device(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+ROW_MAJOR, PANELS = B.DM_W_ROW_MAJOR, B.DM_W_PANELS
+LAYOUTS = (ROW_MAJOR, PANELS)
+LAYOUT_IDS = ("rowmajor", "panels")
+
+
+def pack_reference(W: np.ndarray) -> np.ndarray:
+    """The panel order of include/dm_verify.h, written out with numpy
+    (a layout permutation only), as raw bytes."""
+    V, d = W.shape
+    raw = np.ascontiguousarray(W).view(np.uint8).reshape(V, -1)
+    row_bytes = raw.shape[1]
+    nkb = row_bytes // 64
+    n_panels = -(-V // 64)
+    padded = np.zeros((n_panels * 64, row_bytes), np.uint8)
+    padded[:V] = raw
+    # [panel, g, r16, kb, a, 16 bytes] -> [panel, kb, g, a, r16, 16 bytes]
+    x = padded.reshape(n_panels, 4, 16, nkb, 4, 16)
+    return np.ascontiguousarray(x.transpose(0, 3, 1, 4, 2, 5)).reshape(-1)
+
+
 class Inputs:
     """Device copies of one workload's tensors."""
 
     def __init__(self, W, h, draft, q_hat):
+        self._packed = None
         self.W = to_device(W)
         self.h = to_device(h)
         self.draft = to_device(np.ascontiguousarray(draft, dtype=np.int32))
@@ -61,10 +82,19 @@ def make_verifier(W, h, K, max_batch=None):
     return B.Verifier(d=d, vocab=V, max_batch=max_batch or Bsz, gamma=T1 - 1, k_max=max(K, 1), dtype=dtype)
 
 
-def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True):
+def weights(ver, inp: Inputs, layout):
+    if layout == PANELS:
+        if inp._packed is None:
+            inp._packed = ver.pack_w(inp.W)
+        return inp._packed
+    return inp.W
+
+
+def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR):
     import torch
 
-    out = ver.run(inp.W, inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug)
+    out = ver.run(weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug,
+                  w_layout=layout)
     torch.cuda.synchronize()
     res = {}
     for k, v in out.items():

@@ -9,18 +9,17 @@
 #include <vector>
 
 namespace dmv {
-hipError_t launch_prep(const Plan&, const void*, void*, uint32_t*, hipStream_t) { return hipSuccess; }
-hipError_t launch_gemm(const Plan&, const void*, const void*, float*, Stat*, hipStream_t) { return hipSuccess; }
-hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*, float*, int32_t*, float*,
-                          hipStream_t) { return hipSuccess; }
-hipError_t launch_js(const Plan&, const float*, const float*, const RowStat*, const RowStat*, float*, hipStream_t) {
+hipError_t launch_prep(const Plan&, const void*, void*, RowMeta*, uint32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_pack_w(const void*, void*, int, int, size_t, hipStream_t) { return hipSuccess; }
+hipError_t launch_gemm(const Plan&, const void*, const void*, const RowMeta*, float*, Stat*, hipStream_t) {
     return hipSuccess;
 }
-hipError_t launch_decide(const Plan&, const int32_t*, const float*, const float*, const RowStat*, const RowStat*,
-                         const float*, int32_t*, int32_t*, unsigned long long*, uint8_t*, float*, float*,
-                         hipStream_t) { return hipSuccess; }
-hipError_t launch_race(const Plan&, const float*, const float*, const RowStat*, const int32_t*, unsigned long long*,
-                       int32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*, float*, int32_t*, float*,
+                          hipStream_t) { return hipSuccess; }
+hipError_t launch_vocab(const Plan&, const int32_t*, const float*, const float*, const RowStat*, const RowStat*,
+                        float*, unsigned long long*, int32_t*, int32_t*, uint8_t*, float*, float*, hipStream_t) {
+    return hipSuccess;
+}
 hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipSuccess; }
 int skinny_strips_per_group() { return 32; }
 }  // namespace dmv
@@ -34,7 +33,7 @@ static int fails = 0;
         }                                              \
     } while (0)
 
-static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K, unsigned seed) {
+static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K, unsigned seed, int wp) {
     dm_verify_desc D{d, V, maxB, gamma, kmax, DM_DTYPE_BF16};
     std::vector<uint8_t> modes(B);
     unsigned s = seed;
@@ -48,7 +47,7 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
         nj += modes[b] == DM_MODE_JS_MAJORITY;
     }
     Plan P{};
-    make_plan(D, B, K, nl, nj, P);
+    make_plan(D, B, K, nl, nj, wp, P);
     for (int b = 0; b < B; ++b) {
         if (modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
@@ -56,12 +55,21 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     Sizes sz = workspace_sizes(D);
     const int T1 = gamma + 1;
     CHECK((size_t)P.R_phys * d * 2 <= sz.hm, "Hm overflow\n");
+    CHECK((size_t)P.R_phys * sizeof(RowMeta) <= sz.meta, "row metadata overflow\n");
+    CHECK(!wp || (P.n_vgroups == P.n_panels && (long long)P.n_panels * 64 >= V && P.nkb * 64 == d * 2),
+          "panel split\n");
+    // packed Hm: the last fragment of the last tile ends exactly at R_phys rows
+    CHECK((size_t)P.n_tiles * P.nkb * P.msub * 1024 == (size_t)P.R_phys * d * 2, "packed Hm size\n");
     CHECK((size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) <= sz.part, "part overflow\n");
     CHECK((size_t)P.n_js_pos * P.js_chunks * (K + 1) * sizeof(float) <= sz.jspart || P.n_js_pos == 0,
           "jspart overflow\n");
     CHECK(P.GR * P.ppg <= 64 && P.MT <= 64 && P.ppg >= 1, "tile shape\n");
-    CHECK((long long)P.js_chunks * P.js_chunk >= V && (long long)P.race_chunks * P.race_chunk >= V, "chunks\n");
-    CHECK((P.V + 15) / 16 <= (long long)P.n_vgroups * 32, "vocab groups\n");
+    CHECK(P.n_js_pos == 0 || ((long long)P.js_chunks * P.js_chunk >= V && (long long)(P.js_chunks - 1) * P.js_chunk < V),
+          "js chunks\n");
+    CHECK(nl == 0 || ((long long)P.race_chunks * P.race_chunk >= V && (long long)(P.race_chunks - 1) * P.race_chunk < V),
+          "race chunks\n");
+    CHECK(P.blk_js == P.n_js_pos * P.js_chunks && P.blk_race == nl * P.race_chunks, "block count\n");
+    CHECK(gamma <= 32, "gamma beyond the finishing kernel's JS table\n");
     std::vector<int> seen((size_t)B * T1 * K, 0);
     for (int rho = 0; rho < P.R_phys; ++rho) {
         RowInfo ri = row_info(P, rho);
@@ -115,13 +123,18 @@ int main() {
             for (int B : {1, 2, 7, 32, 64, 200, 256})
                 for (int gamma : {0, 4, 7, 31})
                     for (unsigned seed : {0u, 1u, 2u, 3u}) {
-                        check_case(512, 5003, 256, gamma, kmax, B, K, seed);
-                        ++cases;
+                        for (int wp = 0; wp <= 1; ++wp) {
+                            check_case(512, 5003, 256, gamma, kmax, B, K, seed, wp);
+                            ++cases;
+                        }
                     }
         }
-    check_case(8192, 128256, 32, 7, 5, 32, 5, 0);
-    check_case(5120, 151936, 64, 5, 8, 64, 8, 2);
-    check_case(4096, 128256, 1, 7, 5, 1, 5, 0);
-    std::printf("%d cases, %d failures\n", cases + 3, fails);
+    for (int wp = 0; wp <= 1; ++wp) {
+        check_case(8192, 128256, 32, 7, 5, 32, 5, 0, wp);
+        check_case(5120, 151936, 64, 5, 8, 64, 8, 2, wp);
+        check_case(4096, 128256, 1, 7, 5, 1, 5, 0, wp);
+        cases += 3;
+    }
+    std::printf("%d cases, %d failures\n", cases, fails);
     return fails ? 1 : 0;
 }

@@ -64,7 +64,7 @@ def args(B_=2, K=5, modes=(B.DM_MODE_JS_MAJORITY, B.DM_MODE_NAIVE), **kw):
     fake = 0x10000  # never dereferenced: dm_verify_check does not touch memory
     a.W = a.h = a.draft = a.q_hat = fake
     a.modes = modes_np.ctypes.data if modes is not None else None
-    a.batch, a.K, a.p_drop, a.reserved, a.seed = B_, K, 0.2, 0, 7
+    a.batch, a.K, a.p_drop, a.w_layout, a.seed = B_, K, 0.2, 0, 7
     a.accept_len = a.out_token = fake
     for k, v in kw.items():
         setattr(a, k, v)
@@ -107,7 +107,7 @@ def test_bad_desc(lib, field, value, status):
     (dict(p_drop=1.0), B.DM_ERR_INVALID_ARGUMENT),
     (dict(p_drop=-0.1), B.DM_ERR_INVALID_ARGUMENT),
     (dict(p_drop=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
-    (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(w_layout=2), B.DM_ERR_INVALID_ARGUMENT),
     (dict(W=None), B.DM_ERR_INVALID_ARGUMENT),
     (dict(h=None), B.DM_ERR_INVALID_ARGUMENT),
     (dict(draft=None), B.DM_ERR_INVALID_ARGUMENT),
@@ -156,3 +156,25 @@ def test_status_strings(lib):
     for s in range(5):
         assert B.dm_verify_status_string(s) not in ("", "unknown status")
     assert B.dm_verify_status_string(99) == "unknown status"
+
+
+def test_packed_w_bytes(lib):
+    # ceil(vocab / 64) panels x (row bytes / 64) fragments x 4 strips x 1 KiB
+    assert B.dm_verify_packed_w_bytes(desc(vocab=1000, d=256)) == 16 * (512 // 64) * 4 * 1024
+    assert B.dm_verify_packed_w_bytes(desc(vocab=128256, d=4096)) == 2004 * 128 * 4096
+    assert B.dm_verify_packed_w_bytes(desc(vocab=64, d=64, dtype=B.DM_DTYPE_F32)) == 1 * 4 * 4 * 1024
+    assert B.dm_verify_packed_w_bytes(desc(d=100)) == 0
+
+
+def test_pack_w_rejects_bad_arguments_on_the_host(lib):
+    d = desc()
+    buf = ctypes.create_string_buffer(64)
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert lib.dm_verify_pack_w(ctypes.byref(d), None, ctypes.c_void_p(base), None) == B.DM_ERR_INVALID_ARGUMENT
+    assert lib.dm_verify_pack_w(ctypes.byref(d), ctypes.c_void_p(base), None, None) == B.DM_ERR_INVALID_ARGUMENT
+    assert lib.dm_verify_pack_w(ctypes.byref(d), ctypes.c_void_p(base + 4), ctypes.c_void_p(base),
+                                None) == B.DM_ERR_UNSUPPORTED
+    assert lib.dm_verify_pack_w(None, ctypes.c_void_p(base), ctypes.c_void_p(base), None) == B.DM_ERR_INVALID_ARGUMENT
+    bad = desc(d=100)
+    assert lib.dm_verify_pack_w(ctypes.byref(bad), ctypes.c_void_p(base), ctypes.c_void_p(base),
+                                None) == B.DM_ERR_UNSUPPORTED

@@ -1,8 +1,8 @@
 """GPU parity at the five workloads' full sizes.
 
-Each test runs the library twice on the same inputs: once exactly as
-bench.py times it (no inspection outputs), once with every inspection output
-on.  The oracle evaluates whole sequences (a sequence's outputs depend only
+Each test runs the library on the same inputs with W in both orders
+(row-major and panels), each twice: once exactly as bench.py times it (no
+inspection outputs), once with every inspection output on.  The oracle evaluates whole sequences (a sequence's outputs depend only
 on its own rows), all of them for B = 1 and a sample for the batched
 workloads; both GPU runs must agree with it."""
 import numpy as np
@@ -31,13 +31,14 @@ def _full(cfg_index, seqs, p_values=None, seeds=(None,)):
         for seed in seeds:
             seed = wl.perf_seed(cfg.index) if seed is None else seed
             print(f"  p_drop={p} seed={seed:#x} oracle sequences={list(seqs)}", flush=True)
-            g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False)
-            g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True)
-            np.testing.assert_array_equal(g_bench["accept_len"], g_dbg["accept_len"])
-            np.testing.assert_array_equal(g_bench["out_token"], g_dbg["out_token"])
             o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs)
-            rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
-            rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
+            for layout in P.LAYOUTS:
+                g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=layout)
+                g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=layout)
+                np.testing.assert_array_equal(g_bench["accept_len"], g_dbg["accept_len"])
+                np.testing.assert_array_equal(g_bench["out_token"], g_dbg["out_token"])
+                rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
+                rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
     ver.close()
     print(rep, flush=True)
     return rep

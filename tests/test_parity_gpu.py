@@ -15,13 +15,19 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None):
+@pytest.fixture(params=P.LAYOUTS, ids=P.LAYOUT_IDS)
+def layout(request):
+    return request.param
+
+
+def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None, layout=P.ROW_MAJOR):
     ver = P.make_verifier(W, h, K, max_batch)
     inp = P.Inputs(W, h, draft, q)
     rep = P.Report()
     for seed in seeds:
-        print(f"  seed={seed} B={h.shape[0]} K={K} p={p} modes={np.bincount(modes, minlength=3)}", flush=True)
-        g = P.run_gpu(ver, inp, modes, K, p, seed)
+        print(f"  seed={seed} B={h.shape[0]} K={K} p={p} modes={np.bincount(modes, minlength=3)} layout={layout}",
+              flush=True)
+        g = P.run_gpu(ver, inp, modes, K, p, seed, layout=layout)
         o = P.oracle_run(W, h, draft, q, modes, K, p, seed)
         rep.add(P.compare(g, o, modes, K))
     ver.close()
@@ -33,37 +39,62 @@ def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None):
 
 # ------------------------------------------------------------- tiny config
 @pytest.mark.parametrize("mode", [wl.LOSSLESS, wl.NAIVE, wl.JS], ids=["lossless", "naive", "js"])
-def test_tiny_config_each_mode(mode):
+def test_tiny_config_each_mode(mode, layout):
     w = wl.generate(0)
     modes = np.full(w.cfg.B, mode, np.uint8)
-    rep = _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 21))
+    rep = _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 21), layout=layout)
     assert rep.decision_near_ties <= max(1, rep.decisions // 1000)
 
 
-def test_tiny_shapes_batched_mixed_modes():
+def test_tiny_shapes_batched_mixed_modes(layout):
     """Config-0 shapes with 24 sequences of mixed rules: several GEMM tiles."""
     w = wl.generate(0, B=24)
     modes = np.random.default_rng(3).integers(0, 3, 24).astype(np.uint8)
-    _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 4))
+    _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, w.p_drop, range(1, 4), layout=layout)
 
 
 # ------------------------------------------------- bf16, ragged vocabulary
 @pytest.mark.parametrize("K", [1, 3, 5, 8])
-def test_bf16_ragged_vocab_mixed(K):
+def test_bf16_ragged_vocab_mixed(K, layout):
     """bf16 inputs, |V| not a multiple of 16, several tiles, all three rules."""
     w = wl.generate(2, B=12, gamma=5, d=512, V=5003, K=K, planted=0.7)
     modes = np.array([0, 1, 2] * 4, np.uint8)
-    _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.25, range(1, 4))
+    _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.25, range(1, 4), layout=layout)
 
 
-def test_bf16_lossless_only_and_naive_only():
+@pytest.mark.parametrize("B,gamma,K", [(1, 7, 5), (1, 3, 13), (2, 4, 3), (1, 0, 5)])
+def test_bf16_one_tile_shapes(B, gamma, K, layout):
+    """Shapes whose rows fit one tile (the B = 1 regime), |V| a panel multiple
+    and not, every rule."""
+    for V in (4096, 4099):
+        w = wl.generate(1, B=B, gamma=gamma, d=1024, V=V, K=K, planted=0.8)
+        modes = np.array([2, 0, 1][:B], np.uint8) if B < 3 else np.arange(B, dtype=np.uint8) % 3
+        _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.2, range(1, 4), layout=layout)
+        _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.LOSSLESS, np.uint8), K, 0.2, [9], layout=layout)
+
+
+def test_bf16_lossless_only_and_naive_only(layout):
     w = wl.generate(1, B=9, gamma=3, d=256, V=3001, K=4, planted=0.9)
     for m in (wl.LOSSLESS, wl.NAIVE):
-        _check(w.W, w.h, w.draft, w.q_hat, np.full(9, m, np.uint8), 4, 0.3, range(5, 8))
+        _check(w.W, w.h, w.draft, w.q_hat, np.full(9, m, np.uint8), 4, 0.3, range(5, 8), layout=layout)
+
+
+@pytest.mark.parametrize("dtype_cfg,V,d", [(0, 1000, 256), (1, 1000, 320), (1, 130, 64)])
+def test_pack_w_matches_the_documented_order(dtype_cfg, V, d):
+    """dm_verify_pack_w writes exactly the panel order the header defines."""
+    import torch
+
+    w = wl.generate(dtype_cfg, B=1, gamma=1, d=d, V=V, K=1)
+    ver = P.make_verifier(w.W, w.h, 1)
+    inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
+    got = ver.pack_w(inp.W)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), P.pack_reference(w.W))
+    ver.close()
 
 
 # ----------------------------------------------------------- edge cases
-def test_greedy_reduction_k1_no_dropout():
+def test_greedy_reduction_k1_no_dropout(layout):
     """K = 1, p_drop = 0: the lossy rules are exact match against argmax(W h)."""
     w = wl.generate(2, B=16, gamma=4, d=256, V=2000, K=1, planted=0.5)
     target = (wl.as_f32(w.h).astype(np.float64) @ wl.as_f32(w.W).astype(np.float64).T).argmax(-1)
@@ -71,7 +102,7 @@ def test_greedy_reduction_k1_no_dropout():
     for mode in (wl.NAIVE, wl.JS):
         modes = np.full(16, mode, np.uint8)
         ver = P.make_verifier(w.W, w.h, 1)
-        g = P.run_gpu(ver, P.Inputs(w.W, w.h, draft, w.q_hat), modes, 1, 0.0, 9)
+        g = P.run_gpu(ver, P.Inputs(w.W, w.h, draft, w.q_hat), modes, 1, 0.0, 9, layout=layout)
         match = draft == target[:, :-1]
         np.testing.assert_array_equal(g["accept_flags"].astype(bool), match)
         A = np.where(match.all(1), match.shape[1], np.argmin(match, axis=1))
@@ -80,12 +111,12 @@ def test_greedy_reduction_k1_no_dropout():
         ver.close()
 
 
-def test_gamma_zero():
+def test_gamma_zero(layout):
     w = wl.generate(0, B=4, gamma=0)
-    _check(w.W, w.h, w.draft, w.q_hat, np.array([0, 1, 2, 0], np.uint8), 5, 0.2, [3])
+    _check(w.W, w.h, w.draft, w.q_hat, np.array([0, 1, 2, 0], np.uint8), 5, 0.2, [3], layout=layout)
 
 
-def test_invalid_drafts_and_zero_q():
+def test_invalid_drafts_and_zero_q(layout):
     w = wl.generate(0, B=6, gamma=4)
     draft = w.draft.copy()
     draft[0, 0] = -5
@@ -95,20 +126,21 @@ def test_invalid_drafts_and_zero_q():
     q[2, :, draft[2]] = 0.0
     q[3, 1, draft[3, 1]] = 0.0  # q(x) = 0: kept iff p(x) > 0
     modes = np.array([0, 2, 0, 0, 1, 2], np.uint8)
-    _check(w.W, w.h, draft, q, modes, 5, 0.2, [1, 2])
+    _check(w.W, w.h, draft, q, modes, 5, 0.2, [1, 2], layout=layout)
 
 
-def test_determinism_same_seed_same_outputs():
+def test_determinism_same_seed_same_outputs(layout):
     import torch
 
     w = wl.generate(2, B=8, gamma=5, d=512, V=4096, K=5)
     modes = np.array([0, 1, 2, 2, 1, 0, 2, 2], np.uint8)
     ver = P.make_verifier(w.W, w.h, 5)
     inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
-    a = P.run_gpu(ver, inp, modes, 5, 0.2, 77)
+    a = P.run_gpu(ver, inp, modes, 5, 0.2, 77, layout=layout)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        out = ver.run(inp.W, inp.h, inp.draft, inp.q_hat, modes, 5, 0.2, 77, debug=True)
+        out = ver.run(P.weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, 5, 0.2, 77, debug=True,
+                      w_layout=layout)
     torch.cuda.synchronize()
     for k in a:
         np.testing.assert_array_equal(a[k], out[k].cpu().numpy().view(a[k].dtype), err_msg=k)
