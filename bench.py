@@ -14,7 +14,6 @@ another of the five workloads for inspection.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,7 +26,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_philox_amd", "csrc", "dm_kernels.hip")
 
 
 class HipEvents:
@@ -70,13 +68,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-
-
 def measured_traffic(workload: str):
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
+    of this workload, if it was taken on the current kernel source."""
+    from speculative_decoding_verification_philox_amd.rocprof_summary import kernel_source_hash
+
     path = os.path.join(PROFILES, f"k_gemm_{workload}_traffic.json")
     if not os.path.exists(path):
         return None

@@ -1,0 +1,136 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+  python -m speculative_decoding_verification_philox_amd.rocprof_summary stats \
+      RUN_kernel_stats.csv --command "..." --title "..." > profiles/X.md
+
+  python -m speculative_decoding_verification_philox_amd.rocprof_summary traffic \
+      --fetch FETCH_counter_collection.csv --write WRITE_counter_collection.csv \
+      --kernel k_gemm_panel --workload llama3_8b_head --alg-bytes N \
+      --calib-kernel __amd_rocclr_copyBuffer --calib-bytes 1073741824 \
+      --command "..." --json profiles/k_gemm_llama3_8b_head_traffic.json > profiles/Y.md
+
+`traffic` turns the per-dispatch FETCH_SIZE / WRITE_SIZE counters (KiB) of a
+kernel into HBM bytes per launch.  Each counter is scaled by the factor that
+makes it read the known size of a plain copy kernel captured in the same run
+(bytes read = bytes written = --calib-bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(PKG, "csrc", "dm_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    return re.sub(r"\(.*", "", name).strip()
+
+
+def stats(args) -> None:
+    rows = list(csv.DictReader(open(args.csv)))
+    print(f"# {args.title}\n")
+    print(f"Command (from the repository root):\n\n```\n{args.command}\n```\n")
+    print("| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    print(f"\nKernel source sha256 (first 16 hex digits): `{kernel_source_hash()}`")
+
+
+def _per_dispatch(path: str) -> dict[str, list[float]]:
+    out: dict[str, list[float]] = {}
+    for r in csv.DictReader(open(path)):
+        out.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _match(table: dict[str, list[float]], key: str) -> list[float]:
+    hits = [v for k, v in table.items() if key in k]
+    if len(hits) != 1:
+        raise SystemExit(f"kernel name '{key}' matches {len(hits)} entries: {sorted(table)}")
+    return hits[0]
+
+
+def traffic(args) -> None:
+    fetch, write = _per_dispatch(args.fetch), _per_dispatch(args.write)
+    cf = max(_match(fetch, args.calib_kernel))  # the large copy (the runtime may add tiny ones)
+    cw = max(_match(write, args.calib_kernel))
+    f_scale = args.calib_bytes / (cf * 1024.0)
+    w_scale = args.calib_bytes / (cw * 1024.0)
+    kf = _match(fetch, args.kernel)
+    kw = _match(write, args.kernel)
+    fetch_b = statistics.mean(kf) * 1024.0 * f_scale
+    write_b = statistics.mean(kw) * 1024.0 * w_scale
+    total = fetch_b + write_b
+    rec = {
+        "kernel": args.kernel,
+        "workload": args.workload,
+        "fetch_kib_per_dispatch": [round(x, 1) for x in kf],
+        "write_kib_per_dispatch": [round(x, 1) for x in kw],
+        "calibration": {"kernel": args.calib_kernel, "bytes": args.calib_bytes, "fetch_kib": cf, "write_kib": cw,
+                        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)},
+        "hbm_read_bytes_per_launch": round(fetch_b),
+        "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(total),
+        "algorithmic_bytes_per_launch": args.alg_bytes,
+        "traffic_over_algorithmic": round(total / args.alg_bytes, 4) if args.alg_bytes else None,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "command": args.command,
+    }
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    print(f"# HBM traffic of `{args.kernel}`, {args.workload}\n")
+    print(f"Commands (from the repository root, one run per counter):\n\n```\n{args.command}\n```\n")
+    print(f"Calibration: `{args.calib_kernel}` copies {args.calib_bytes} bytes.  The counters read "
+          f"FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB, so the scale factors are "
+          f"{f_scale:.4f} (read) and {w_scale:.4f} (write).\n")
+    print("| quantity | per launch |")
+    print("|---|---|")
+    print(f"| FETCH_SIZE (KiB, raw, per dispatch) | {', '.join(f'{x:.1f}' for x in kf)} |")
+    print(f"| WRITE_SIZE (KiB, raw, per dispatch) | {', '.join(f'{x:.1f}' for x in kw)} |")
+    print(f"| HBM read bytes (scaled) | {fetch_b:,.0f} |")
+    print(f"| HBM write bytes (scaled) | {write_b:,.0f} |")
+    print(f"| HBM bytes total | {total:,.0f} |")
+    print(f"| algorithmic bytes | {args.alg_bytes:,} |")
+    if args.alg_bytes:
+        print(f"| traffic / algorithmic | {total / args.alg_bytes:.4f} |")
+    print(f"\nKernel source sha256 (first 16 hex digits): `{kernel_source_hash()}`")
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--alg-bytes", type=int, required=True)
+    t.add_argument("--calib-kernel", default="__amd_rocclr_copyBuffer")
+    t.add_argument("--calib-bytes", type=int, default=1 << 30)
+    t.add_argument("--command", required=True)
+    t.add_argument("--json", default=None)
+    a = ap.parse_args(argv)
+    {"stats": stats, "traffic": traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
