@@ -148,16 +148,19 @@ void dmo_row_stats(const double* l, int n, double* out_max, double* out_logz,
 
 /* Jensen-Shannon divergence, natural log ([DM] Eq. (6); the paper does not
  * define JS, the reading is the standard divergence with M = (P + Q) / 2 and
- * 0 ln 0 = 0).  P and Q are used as given (not renormalised). */
+ * 0 ln 0 = 0).  P and Q are used as given (not renormalised).  ln M is taken
+ * as ln(P + Q) - ln 2, which never forms a halved subnormal that could round
+ * to zero. */
 double dmo_js(const double* P, const double* Q, int n)
 {
     double acc = 0.0;
     for (int v = 0; v < n; ++v) {
         double p = P[v], q = Q[v];
-        double mix = 0.5 * (p + q);
+        if (!(p + q > 0.0)) continue;
+        double log_mix = log(p + q) - log(2.0);
         double term = 0.0;
-        if (p > 0.0) term += p * log(p / mix);
-        if (q > 0.0) term += q * log(q / mix);
+        if (p > 0.0) term += p * (log(p) - log_mix);
+        if (q > 0.0) term += q * (log(q) - log_mix);
         acc += term;
     }
     return 0.5 * acc;
