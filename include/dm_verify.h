@@ -88,7 +88,7 @@ typedef enum dm_mode {
 /* Problem limits fixed at handle creation. */
 typedef struct dm_verify_desc {
     int32_t d;         /* hidden size; multiple of 64, 64..65536 */
-    int32_t vocab;     /* |V|, 1..2^24 */
+    int32_t vocab;     /* |V|, 1..524288 */
     int32_t max_batch; /* largest B a run may pass, 1..256 */
     int32_t gamma;     /* drafted tokens per sequence, 0..31 (gamma+1 positions) */
     int32_t k_max;     /* largest K a run may pass, 1..16 */

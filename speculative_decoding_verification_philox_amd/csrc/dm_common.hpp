@@ -55,6 +55,7 @@ struct Plan {
     int n_vgroups;
     // vocabulary pass: JS blocks, then race blocks
     int n_js_pos, js_chunks, js_chunk;
+    int vec4;  // logits and q_hat rows are 16-byte aligned (V % 4 == 0)
     int race_chunks, race_chunk;
     int blk_js, blk_race;
 };

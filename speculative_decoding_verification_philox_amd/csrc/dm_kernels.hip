@@ -132,31 +132,82 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ W, u
 // =====================================================================
 // k_gemm_panel: L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j]
 // (DropMatch Eq. (3), the shared head W) for one tile of up to 64 rows and
-// one panel of 64 vocabulary rows per wave, W in panel order.
+// one panel of 64 vocabulary rows per wave, W in panel order; a workgroup's
+// four waves take four neighbouring panels of one tile.
 //
 // Main loop: the wave streams its panel front to back, 1 KiB per load
 // instruction (non-temporal: W is read once), four strips of 16 vocabulary
 // rows per 64-byte fragment; the tile's masked rows come from the packed Hm
 // (L2-resident, shared by every wave).  The next fragment's loads are in
 // flight while the current one feeds v_mfma_f32_16x16x32_bf16 (16x16x4 for
-// fp32).  No LDS and no barrier anywhere in the kernel.
+// fp32).  No LDS and no barrier in the loop.
 //
 // Epilogue, straight from the accumulators: lane 16 a + c holds column
 // 16 g + c of rows 16 m + 4 a + j.  Rows later passes need are stored; per
 // row, (max, sum exp, argmax) over the panel's 64 columns comes from the
-// lane's four columns and a butterfly over the 16 lanes of its group.  A
+// lane's four columns and DPP reductions over the 16 lanes of its row.  A
 // position's K head rows sit in one lane group (slot layout), so its
 // centroid (the mean of the heads, DropMatch Eq. (5)) is formed in-lane and
-// reduced the same way.  Results go to part[target][panel].
+// reduced the same way.  The four waves' results are merged in panel order
+// through LDS into part[target][panel group].
 // =====================================================================
 constexpr int kPanelWaves = 4;
 constexpr int kPanelStrips = 4;
 constexpr int kPanelNK = 1;  // fragments per pipeline stage
 
-__device__ __forceinline__ Stat stat_reduce16(Stat st) {
+// Reductions over the 16 lanes of a DPP row (lanes 16 a .. 16 a + 15): swap
+// neighbours, then pairs, then mirror within each half row, then within the
+// row; every lane ends with the same value, formed in the same order.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = x + dpp_f<kDppXor1>(x);
+    x = x + dpp_f<kDppXor2>(x);
+    x = x + dpp_f<kDppHalfMirror>(x);
+    return x + dpp_f<kDppMirror>(x);
+}
+__device__ __forceinline__ int row16_min(int x) {
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    return min(x, dpp_i<kDppMirror>(x));
+}
+
+// (max, sum exp, lowest argmax) of the 64 values held as four per lane by
+// the 16 lanes of a row; columns >= V are left out.
+template <int G>
+__device__ __forceinline__ Stat row16_stat(const float (&x)[G], const bool (&ok)[G], int col0) {
+    float m = -INFINITY;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off));
-    return st;
+    for (int g = 0; g < G; ++g)
+        if (ok[g]) m = fmaxf(m, x[g]);
+    m = row16_max(m);
+    float s = 0.0f;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        if (ok[g]) {
+            s += __expf(x[g] - m);
+            if (x[g] == m) idx = min(idx, col0 + 16 * g);
+        }
+    return Stat{m, row16_sum(s), row16_min(idx)};
 }
 
 template <bool BF16, int MSUB>
@@ -166,10 +217,13 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
                                                                  float* __restrict__ logits,
                                                                  Stat* __restrict__ part) {
     constexpr int ROWS = 16 * MSUB, G = kPanelStrips, NK = kPanelNK;
+    constexpr int SLOTS = ROWS + 64;  // rows, then centroid slots (at most 4 groups x 16)
+    __shared__ Stat s_st[kPanelWaves][SLOTS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int gw = blockIdx.x * kPanelWaves + wave;
-    if (gw >= P.n_panels * P.n_tiles) return;  // nothing below synchronises the block
-    const int panel = gw % P.n_panels, tile = gw / P.n_panels;
+    const int tile = blockIdx.y;
+    const int panel_raw = blockIdx.x * kPanelWaves + wave;
+    const bool active = panel_raw < P.n_panels;  // a wave past the last panel only joins the merge
+    const int panel = active ? panel_raw : P.n_panels - 1;
     const int nkb = P.nkb;
 
     // metadata of tile row `lane`, fetched now, read through shuffles later
@@ -181,7 +235,7 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
-    {
+    if (active) {
         const uint8_t* wp = Wp + (size_t)panel * nkb * G * 1024 + lane * 16;
         const uint8_t* ap = Hp + (size_t)tile * nkb * MSUB * 1024 + lane * 16;
         v4u wc[NK][G], ac[NK][MSUB], wn[NK][G], an[NK][MSUB];
@@ -229,6 +283,9 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
     // ---------------- epilogue ----------------
     const int grp = lane >> 4, c = lane & 15;
     const int col0 = panel * 64 + c;
+    bool ok[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) ok[g] = active && col0 + 16 * g < P.V;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
@@ -237,25 +294,29 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
             const float sc = __shfl(my.scale, r, 64);
             const int canon = __shfl(my.canon, r, 64);
             const int store = __shfl(my.store, r, 64);
-            Stat st = stat_empty();
+            float x[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float x = acc[g][m][j] * sc;
-                acc[g][m][j] = x;
-                const int col = col0 + 16 * g;
-                if (col < P.V) {
-                    if (store) logits[(size_t)canon * P.V + col] = x;
-                    stat_push(st, x, col);
-                }
+                x[g] = acc[g][m][j] * sc;
+                acc[g][m][j] = x[g];
             }
-            st = stat_reduce16(st);
-            if (c == 0) part[(size_t)(tile * ROWS + r) * P.n_panels + panel] = st;
+            Stat st = stat_empty();
+            if (canon >= 0) {  // not a padding row (the whole 16-lane row agrees)
+                if (store) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        if (ok[g]) logits[(size_t)canon * P.V + col0 + 16 * g] = x[g];
+                }
+                st = row16_stat<G>(x, ok, col0);
+            }
+            if (c == 0) s_st[wave][r] = st;
         }
-    if (tile < P.tiles_lossy) {
-        const int npt = P.GR * P.ppg;
+    const int npt = P.GR * P.ppg;
+    const bool lossy_tile = tile < P.tiles_lossy;
+    if (lossy_tile) {
         for (int slot = 0; slot < P.ppg; ++slot) {
             const int first = slot * P.K;
-            Stat st = stat_empty();
+            float x[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 // head rows first .. first + K - 1 of this lane group, summed in head order
@@ -268,13 +329,26 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
                         sum = i == 0 ? v : sum + v;
                     }
                 }
-                const int col = col0 + 16 * g;
-                if (col < P.V) stat_push(st, sum * P.inv_k, col);
+                x[g] = sum * P.inv_k;
             }
-            st = stat_reduce16(st);
-            const int p = tile * npt + grp * P.ppg + slot;
-            if (c == 0 && p < P.n_lossy_pos) part[(size_t)(P.R_phys + p) * P.n_panels + panel] = st;
+            const Stat st = row16_stat<G>(x, ok, col0);
+            if (c == 0) s_st[wave][ROWS + grp * P.ppg + slot] = st;
         }
+    }
+    __syncthreads();
+    // merge the workgroup's panels in panel order: part[target][panel group]
+    const int nloc = ROWS + (lossy_tile ? npt : 0);
+    for (int t = threadIdx.x; t < nloc; t += blockDim.x) {
+        Stat st = s_st[0][t];
+#pragma unroll
+        for (int w = 1; w < kPanelWaves; ++w) st = stat_merge(st, s_st[w][t]);
+        int target = tile * ROWS + t;
+        if (t >= ROWS) {
+            const int p = tile * npt + (t - ROWS);
+            if (p >= P.n_lossy_pos) continue;
+            target = P.R_phys + p;
+        }
+        part[(size_t)target * P.n_vgroups + blockIdx.x] = st;
     }
 }
 
@@ -602,19 +676,26 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
 // =====================================================================
 constexpr int kVocabThreads = 256;
 constexpr int kVocabWaves = kVocabThreads / 64;
-constexpr int kJsPerThread = 4;  // the JS chunk is a multiple of kVocabThreads * kJsPerThread
+constexpr int kJsPerThread = 8;  // the JS chunk is kVocabThreads * kJsPerThread entries
 constexpr float kLn2 = 0.69314718055994531f;
 
+// e^x and ln x on the hardware base-2 units (v_exp_f32, v_log_f32), for
+// arguments whose results stay in the normal fp32 range.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float hw_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+
+// Smallest mixture the JS terms evaluate ln of; an entry whose two
+// probabilities sum to less contributes below 1e-36 and is left at that.
+constexpr float kMixFloor = 1e-37f;
+
 // One vocabulary entry's share of JS(P || Q): with a = ln P, b = ln Q and
-// ln M = ln(P + Q) - ln 2, it is (P (a - ln M) + Q (b - ln M)) / 2, where a
-// zero probability contributes nothing.
+// ln M = ln(P + Q) - ln 2, it is (P (a - ln M) + Q (b - ln M)) / 2.  A zero
+// probability contributes nothing as long as its log argument is finite.
+// Branch-free.
 __device__ __forceinline__ float js_entry(float a, float Pa, float b, float Pb) {
-    const float sum = Pa + Pb;
-    if (!(sum > 0.0f)) return 0.0f;
-    const float lm = __logf(sum) - kLn2;
-    const float ta = Pa > 0.0f ? Pa * (a - lm) : 0.0f;
-    const float tb = Pb > 0.0f ? Pb * (b - lm) : 0.0f;
-    return 0.5f * (ta + tb);
+    const float lm = hw_log(fmaxf(Pa + Pb, kMixFloor)) - kLn2;
+    return 0.5f * (Pa * (a - lm) + Pb * (b - lm));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -664,6 +745,103 @@ __device__ __forceinline__ int first_reject(bool reject, int G) {
     return rej ? __ffsll((long long)rej) - 1 : G;
 }
 
+// JS partial sums of one (position, chunk): kJsPerThread consecutive entries
+// per thread, every load issued before any arithmetic (float4 loads when
+// rows are 16-byte aligned).  KMAX bounds K so the registers stay small.
+template <int KMAX>
+__device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __restrict__ q_hat,
+                                         const float* __restrict__ logits, const RowStat* __restrict__ rowstat,
+                                         const RowStat* __restrict__ centstat, float* __restrict__ jspart,
+                                         float (*s_red)[kMaxK + 1]) {
+    constexpr int E = kJsPerThread;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = P.K, G = P.G, T1 = P.T1, V = P.V;
+    const int jp = blk / P.js_chunks, c = blk - jp * P.js_chunks;
+    const int js_rank = jp / G, t = jp - js_rank * G;
+    const int b = select_of(P.js_bits, P.B, js_rank, true);
+    const int pidx = b * T1 + t;
+    const float* lrow = logits + (size_t)pidx * K * V;
+    const float* qrow = q_hat + (size_t)(b * G + t) * V;
+    const int v0 = c * P.js_chunk + threadIdx.x * E;
+
+    // Loads past the end of the vocabulary read a valid entry instead and are
+    // zeroed, so no lane branches; q = -1 marks them.
+    float l[E][KMAX], q[E];
+    if (P.vec4) {
+#pragma unroll
+        for (int u = 0; u < E; u += 4) {
+            const bool ok = v0 + u < V;  // V % 4 == 0: a float4 is wholly in or out
+            const int vv = ok ? v0 + u : V - 4;
+#pragma unroll
+            for (int i = 0; i < KMAX; ++i) {
+                v4f x = v4f{0.f, 0.f, 0.f, 0.f};
+                if (i < K) x = *(const v4f*)(lrow + (size_t)i * V + vv);  // K is uniform
+#pragma unroll
+                for (int e = 0; e < 4; ++e) l[u + e][i] = ok ? x[e] : 0.0f;
+            }
+            const v4f y = *(const v4f*)(qrow + vv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[u + e] = ok ? y[e] : -1.0f;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+            const bool ok = v0 + u < V;
+            const int vv = ok ? v0 + u : V - 1;
+#pragma unroll
+            for (int i = 0; i < KMAX; ++i) {
+                float x = 0.0f;
+                if (i < K) x = lrow[(size_t)i * V + vv];
+                l[u][i] = ok ? x : 0.0f;
+            }
+            const float y = qrow[vv];
+            q[u] = ok ? y : -1.0f;
+        }
+    }
+    float logz[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) logz[i] = i < K ? rowstat[pidx * K + i].logz : 0.0f;
+    const float logz_c = centstat[pidx].logz;
+
+    float acc[KMAX + 1];
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const float live = q[u] < 0.0f ? 0.0f : 1.0f;  // 0 past the end of the vocabulary
+        // the centroid logit, same operations in the same order as the
+        // LM-head epilogue's
+        float lsum = l[u][0];
+#pragma unroll
+        for (int i = 1; i < KMAX; ++i)
+            if (i < K) lsum += l[u][i];
+        const float bb = lsum * P.inv_k - logz_c;
+        const float pb = hw_exp(bb) * live;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+            if (i < K) {
+                const float a = l[u][i] - logz[i];
+                acc[i] += js_entry(a, hw_exp(a) * live, bb, pb);
+            }
+        const float qq = fmaxf(q[u], 0.0f);
+        acc[KMAX] += js_entry(hw_log(fmaxf(qq, kMixFloor)), qq, bb, pb);
+    }
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i)
+        if (i < K || i == KMAX) {
+            const float x = wave_sum(acc[i]);
+            if (lane == 0) s_red[wave][i == KMAX ? kMaxK : i] = x;
+        }
+    __syncthreads();
+    if (threadIdx.x <= K) {
+        const int i = threadIdx.x == K ? kMaxK : threadIdx.x;
+        float x = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kVocabWaves; ++w) x += s_red[w][i];
+        jspart[((size_t)jp * (K + 1) + threadIdx.x) * P.js_chunks + c] = x;
+    }
+}
+
 __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const Plan P, const int32_t* __restrict__ draft, const float* __restrict__ q_hat,
     const float* __restrict__ logits, const RowStat* __restrict__ rowstat, const RowStat* __restrict__ centstat,
@@ -673,68 +851,13 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = P.K, G = P.G, T1 = P.T1, V = P.V;
     int blk = blockIdx.x;
+    (void)wave;
 
     if (blk < P.blk_js) {
-        const int jp = blk / P.js_chunks, c = blk - jp * P.js_chunks;
-        const int js_rank = jp / G, t = jp - js_rank * G;
-        const int b = select_of(P.js_bits, P.B, js_rank, true);
-        const int pidx = b * T1 + t;
-        float logz[kMaxK];
-#pragma unroll
-        for (int i = 0; i < kMaxK; ++i) logz[i] = i < K ? rowstat[pidx * K + i].logz : 0.0f;
-        const float logz_c = centstat[pidx].logz;
-        float acc[kMaxK + 1];
-#pragma unroll
-        for (int i = 0; i <= kMaxK; ++i) acc[i] = 0.0f;
-        const float* lrow = logits + (size_t)pidx * K * V;
-        const float* qrow = q_hat + (size_t)(b * G + t) * V;
-        // kJsPerThread entries per thread, all loads issued before any use
-        const int vb = c * P.js_chunk + threadIdx.x;
-        for (int u0 = 0; u0 < P.js_chunk / kVocabThreads; u0 += kJsPerThread) {
-            float l[kJsPerThread][kMaxK];
-            float q[kJsPerThread];
-#pragma unroll
-            for (int u = 0; u < kJsPerThread; ++u) {
-                const int v = vb + (u0 + u) * kVocabThreads;
-                const bool ok = v < V;
-#pragma unroll
-                for (int i = 0; i < kMaxK; ++i) l[u][i] = (i < K && ok) ? lrow[(size_t)i * V + v] : 0.0f;
-                q[u] = ok ? qrow[v] : -1.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < kJsPerThread; ++u) {
-                if (q[u] < 0.0f) continue;  // past the end of the vocabulary
-                // the centroid logit, same operations in the same order as
-                // the LM-head epilogue's centroid_logit()
-                float lsum = l[u][0];
-#pragma unroll
-                for (int i = 1; i < kMaxK; ++i)
-                    if (i < K) lsum += l[u][i];
-                const float bb = lsum * P.inv_k - logz_c;
-                const float pb = __expf(bb);
-#pragma unroll
-                for (int i = 0; i < kMaxK; ++i)
-                    if (i < K) {
-                        const float a = l[u][i] - logz[i];
-                        acc[i] += js_entry(a, __expf(a), bb, pb);
-                    }
-                acc[kMaxK] += q[u] > 0.0f ? js_entry(__logf(q[u]), q[u], bb, pb) : js_entry(0.0f, 0.0f, bb, pb);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i <= kMaxK; ++i)
-            if (i < K || i == kMaxK) {
-                const float x = wave_sum(acc[i]);
-                if (lane == 0) s_red[wave][i] = x;
-            }
-        __syncthreads();
-        if (threadIdx.x <= K) {
-            const int i = threadIdx.x == K ? kMaxK : threadIdx.x;
-            float x = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kVocabWaves; ++w) x += s_red[w][i];
-            jspart[((size_t)jp * (K + 1) + threadIdx.x) * P.js_chunks + c] = x;
-        }
+        if (K <= 8)
+            js_block<8>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
+        else
+            js_block<kMaxK>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
         return;
     }
     blk -= P.blk_js;
@@ -790,7 +913,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 }
 
 // =====================================================================
-// k_finish: one wave per sequence.  Applies the sequence's rule at every
+// k_finish: one block per sequence.  Applies the sequence's rule at every
 // drafted position (lane t decides position t), finds the first rejection A
 // ("Speculative Decoding: Draft, Then Verify", the draft-then-verify loop,
 // steps 3 and 4) and emits one token: the centroid argmax at A for the
@@ -798,7 +921,11 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 // it then clears for the next call).  JS sums over the vocabulary chunks
 // are reduced here in a fixed order.
 // =====================================================================
-__global__ __launch_bounds__(64) void k_finish(const Plan P, const int32_t* __restrict__ draft,
+constexpr int kFinishWaves = 4;
+constexpr int kFinishBatch = 4;
+constexpr int kFinishPerLane = 4;  // JS chunks per lane: up to 256 chunks per position
+
+__global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const Plan P, const int32_t* __restrict__ draft,
                                                const float* __restrict__ q_hat, const float* __restrict__ logits,
                                                const RowStat* __restrict__ rowstat,
                                                const RowStat* __restrict__ centstat,
@@ -808,23 +935,41 @@ __global__ __launch_bounds__(64) void k_finish(const Plan P, const int32_t* __re
                                                uint8_t* __restrict__ dbg_flags, float* __restrict__ dbg_js_heads,
                                                float* __restrict__ dbg_js_draft) {
     __shared__ float s_js[32][kMaxK + 1];
-    const int b = blockIdx.x, lane = threadIdx.x;
+    const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = P.K, G = P.G, T1 = P.T1;
     const bool lossless = bit_of(P.lossless_bits, b);
     const bool js = bit_of(P.js_bits, b);
     if (js && G > 0) {
-        // lane `idx` sums one (position, head-or-draft) over the chunks in
-        // chunk order; partials are laid out [JS position][K + 1][chunk]
+        // wave w sums the (position, head-or-draft) pairs w, w + 4, ... over
+        // the chunks: every load is issued first, then fixed-order sums
+        // (lane-strided, then across the wave)
         const int jp0 = rank_of(P.js_bits, b, true) * G;
-        for (int idx = lane; idx < G * (K + 1); idx += 64) {
-            const float* src = jspart + ((size_t)jp0 * (K + 1) + idx) * P.js_chunks;
-            float x = 0.0f;
-#pragma unroll 8
-            for (int cc = 0; cc < P.js_chunks; ++cc) x += src[cc];
-            s_js[idx / (K + 1)][idx % (K + 1)] = x;
+        const int n_idx = G * (K + 1);
+        for (int base = wave; base < n_idx; base += kFinishWaves * kFinishBatch) {
+            float x[kFinishBatch][kFinishPerLane];
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u) {
+                const int idx = base + u * kFinishWaves;
+                const float* src = jspart + ((size_t)jp0 * (K + 1) + idx) * P.js_chunks;
+#pragma unroll
+                for (int q = 0; q < kFinishPerLane; ++q) {
+                    const int cc = lane + 64 * q;
+                    x[u][q] = (idx < n_idx && cc < P.js_chunks) ? src[cc] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u) {
+                const int idx = base + u * kFinishWaves;
+                float acc = x[u][0];
+#pragma unroll
+                for (int q = 1; q < kFinishPerLane; ++q) acc += x[u][q];
+                const float tot = wave_sum(acc);
+                if (lane == 0 && idx < n_idx) s_js[idx / (K + 1)][idx % (K + 1)] = tot;
+            }
         }
-        __syncthreads();
     }
+    __syncthreads();
+    if (wave != 0) return;
     bool accept = false;
     if (lane < G) {
         if (lossless) {
@@ -884,8 +1029,7 @@ hipError_t launch_pack_w(const void* W, void* Wp, int V, int nkb, size_t n16, hi
 template <bool BF16>
 static hipError_t launch_panel_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
                                  Stat* part, hipStream_t st) {
-    const int work = P.n_panels * P.n_tiles;
-    dim3 grid((work + kPanelWaves - 1) / kPanelWaves), block(kPanelWaves * 64);
+    dim3 grid((P.n_panels + kPanelWaves - 1) / kPanelWaves, P.n_tiles), block(kPanelWaves * 64);
     const uint8_t* w = (const uint8_t*)Wp;
     const uint8_t* a = (const uint8_t*)Hp;
     switch (P.msub) {
@@ -941,7 +1085,8 @@ hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat,
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(64), 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
+    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishWaves * 64), 0, st, P, draft, q_hat, logits, rowstat, centstat,
+                       jspart,
                        race_best, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
 }

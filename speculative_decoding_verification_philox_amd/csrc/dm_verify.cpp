@@ -33,7 +33,9 @@ struct dm_verify {
 
 namespace {
 
-constexpr int kGroupsPerTile = 4;  // 16x16 MFMA output: four row groups per lane
+constexpr int kGroupsPerTile = 4;
+// The vocabulary pass splits a position into at most 256 chunks of 2048.
+constexpr int kMaxVocab = 256 * 2048;  // 16x16 MFMA output: four row groups per lane
 
 int elem_size(int dtype) { return dtype == DM_DTYPE_BF16 ? 2 : 4; }
 
@@ -43,7 +45,7 @@ int check_desc(const dm_verify_desc* D) {
     if (!D) return DM_ERR_INVALID_ARGUMENT;
     if (D->d <= 0 || D->vocab <= 0 || D->max_batch <= 0 || D->gamma < 0 || D->k_max <= 0)
         return DM_ERR_INVALID_ARGUMENT;
-    if (D->max_batch > kMaxBatch || D->gamma > 31 || D->k_max > kMaxK || D->vocab > (1 << 24))
+    if (D->max_batch > kMaxBatch || D->gamma > 31 || D->k_max > kMaxK || D->vocab > kMaxVocab)
         return DM_ERR_INVALID_ARGUMENT;
     if (D->dtype != DM_DTYPE_F32 && D->dtype != DM_DTYPE_BF16) return DM_ERR_UNSUPPORTED;
     if (D->d % 64 != 0 || D->d > 65536) return DM_ERR_UNSUPPORTED;
@@ -128,8 +130,8 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
     P.nkb = (int)((size_t)D.d * elem_size(D.dtype) / 64);
     P.n_panels = cdiv(P.V, 64);
     if (w_packed) {
-        // one wave per (panel, tile); statistic partials per panel
-        P.n_vgroups = P.n_panels;
+        // one wave per (panel, tile); statistic partials per group of four panels
+        P.n_vgroups = cdiv(P.n_panels, 4);
     } else {
         const int nstr = cdiv(P.V, 16);
         const int spg = skinny_strips_per_group();
@@ -138,11 +140,11 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         P.n_vgroups = ng > fill ? ng : fill;
     }
 
-    // vocabulary pass: JS positions split into chunks of 1024 entries (four
+    // vocabulary pass: JS positions split into chunks of 2048 entries (eight
     // per thread of a 256-thread block)
     P.n_js_pos = n_js * P.G;
     P.js_chunks = 0;
-    P.js_chunk = 1024;
+    P.js_chunk = 2048;
     if (P.n_js_pos > 0) P.js_chunks = cdiv(P.V, P.js_chunk);
     P.race_chunks = 0;
     P.race_chunk = P.V;
@@ -332,6 +334,7 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     P.key0 = (uint32_t)(a->seed & 0xffffffffu);
     P.key1 = (uint32_t)(a->seed >> 32);
     P.store_all = a->logits != nullptr;
+    P.vec4 = (D.vocab % 4 == 0) && aligned(a->q_hat, 16) && aligned(a->logits ? (const void*)a->logits : h->logits, 16);
     // The workspace was sized for the worst plan of the desc; refuse a plan
     // that would not fit rather than launch past the end of a buffer.
     if ((size_t)P.R_phys * D.d * elem_size(D.dtype) > h->cap_hm || (size_t)P.R_phys > h->cap_meta_rows ||

@@ -56,7 +56,7 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     const int T1 = gamma + 1;
     CHECK((size_t)P.R_phys * d * 2 <= sz.hm, "Hm overflow\n");
     CHECK((size_t)P.R_phys * sizeof(RowMeta) <= sz.meta, "row metadata overflow\n");
-    CHECK(!wp || (P.n_vgroups == P.n_panels && (long long)P.n_panels * 64 >= V && P.nkb * 64 == d * 2),
+    CHECK(!wp || (P.n_vgroups == (P.n_panels + 3) / 4 && (long long)P.n_panels * 64 >= V && P.nkb * 64 == d * 2),
           "panel split\n");
     // packed Hm: the last fragment of the last tile ends exactly at R_phys rows
     CHECK((size_t)P.n_tiles * P.nkb * P.msub * 1024 == (size_t)P.R_phys * d * 2, "packed Hm size\n");

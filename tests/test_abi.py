@@ -82,7 +82,7 @@ def test_valid_arguments_pass(lib):
     ("d", 96, B.DM_ERR_UNSUPPORTED),
     ("d", 131072, B.DM_ERR_UNSUPPORTED),
     ("vocab", 0, B.DM_ERR_INVALID_ARGUMENT),
-    ("vocab", (1 << 24) + 1, B.DM_ERR_INVALID_ARGUMENT),
+    ("vocab", 524288 + 1, B.DM_ERR_INVALID_ARGUMENT),
     ("max_batch", 0, B.DM_ERR_INVALID_ARGUMENT),
     ("max_batch", 257, B.DM_ERR_INVALID_ARGUMENT),
     ("gamma", -1, B.DM_ERR_INVALID_ARGUMENT),
