@@ -5,6 +5,9 @@
 //   k_gemm_panel  LM-head GEMM over panel-ordered W: one wave streams one
 //                 panel of 64 vocabulary rows straight into MFMA operands,
 //                 with a softmax-statistics epilogue per row and per centroid
+//   k_gemm_tile   the same for many rows: tiles of up to 160 rows, four
+//                 panels per workgroup, loader waves filling an LDS ring for
+//                 compute waves, XCD-aware order
 //   k_gemm_skinny LM-head GEMM over row-major W (all rows of a tile in one
 //                 workgroup; W streamed from HBM straight into MFMA operands),
 //                 same epilogue
@@ -349,6 +352,222 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
             target = P.R_phys + p;
         }
         part[(size_t)target * P.n_vgroups + blockIdx.x] = st;
+    }
+}
+
+// =====================================================================
+// k_gemm_tile: the LM head for many rows (the matrix-core-bound regime):
+// L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] for one tile of
+// 16 * MSUB rows (up to 160) and one group of four panels per workgroup.
+//
+// Warp-specialised: waves 0-3 compute, waves 4-7 load.  The loaders copy
+// each stage (kTileKC fragments of the four panels of W and of the tile's
+// packed Hm) from global memory straight into an LDS ring (direct
+// global-to-LDS loads, 16 bytes per lane, so a fragment is one instruction);
+// the compute waves only read LDS and issue v_mfma_f32_16x16x32_bf16
+// (16x16x4 for fp32), 4 x MSUB per fragment.  One barrier per stage: the
+// loaders have waited for the next stage's loads, the compute waves have
+// finished the stage the loaders refill next.  Blocks are mapped so that
+// the tiles sharing a panel group run together on one XCD (workgroups go to
+// the eight XCDs in turn), where the group's W is read from HBM once and
+// then from that XCD's L2.
+//
+// The epilogue is the panel kernel's, with the row metadata in LDS:
+// statistics per row and per centroid over each compute wave's 64 columns,
+// merged across the four into part[target][panel group]; stored rows
+// written.
+// =====================================================================
+constexpr int kTileComputeWaves = 4;
+constexpr int kTileThreads = 2 * kTileComputeWaves * 64;
+constexpr int kTileKC = 2;    // fragments per LDS stage
+constexpr int kTileNBUF = 2;  // stages in the ring
+
+#define DM_AS_GLOBAL __attribute__((address_space(1)))
+#define DM_AS_LDS __attribute__((address_space(3)))
+
+// s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <bool BF16, int MSUB>
+__global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
+                                                            const uint8_t* __restrict__ Hp,
+                                                            const RowMeta* __restrict__ meta,
+                                                            float* __restrict__ logits,
+                                                            Stat* __restrict__ part) {
+    constexpr int ROWS = 16 * MSUB, G = 4, KC = kTileKC, NBUF = kTileNBUF, CW = kTileComputeWaves;
+    constexpr int WB = CW * KC * G * 1024;  // W bytes per stage (four panels)
+    constexpr int AB = KC * MSUB * 1024;    // masked-row bytes per stage
+    constexpr int NA = KC * MSUB;           // masked-row fragments per stage
+    __shared__ __align__(16) uint8_t ring[NBUF][WB + AB];
+    __shared__ Stat s_st[CW][2 * ROWS];
+    __shared__ RowMeta s_meta[ROWS];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_groups = (P.n_panels + 3) >> 2;
+    const int per_xcd = (n_groups + 7) >> 3;
+    const int xcd = blockIdx.x & 7, k_local = blockIdx.x >> 3;
+    const int group = xcd * per_xcd + k_local / P.n_tiles;
+    const int tile = k_local % P.n_tiles;
+    if (group >= n_groups) return;  // the whole block, before any barrier
+    const int nkb = P.nkb;
+    const int nstage = nkb / KC;  // nkb is even (d is a multiple of 64)
+
+    for (int r = threadIdx.x; r < ROWS; r += blockDim.x) s_meta[r] = meta[(size_t)tile * ROWS + r];
+
+    v4f acc[G][MSUB];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int my_panel = group * 4 + (wave & 3);
+    const bool active = wave < CW && my_panel < P.n_panels;
+
+    if (wave >= CW) {
+        // ---------------- loader waves ----------------
+        const int lw = wave - CW;
+        const int panel = min(group * 4 + lw, P.n_panels - 1);  // a missing panel reads a valid one
+        const uint8_t* wsrc = Wp + (size_t)panel * nkb * G * 1024 + lane * 16;
+        const uint8_t* asrc = Hp + (size_t)tile * nkb * MSUB * 1024 + lane * 16;
+        auto issue = [&](int st) {
+            uint8_t* base = ring[st % NBUF];
+#pragma unroll
+            for (int f = 0; f < KC * G; ++f)
+                __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(wsrc + ((size_t)st * KC * G + f) * 1024),
+                                                 (DM_AS_LDS void*)(base + (lw * KC * G + f) * 1024), 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < (NA + 3) / 4; ++j) {
+                const int f = lw + 4 * j;
+                if (f < NA)
+                    __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(asrc + ((size_t)st * NA + f) * 1024),
+                                                     (DM_AS_LDS void*)(base + WB + f * 1024), 16, 0, 0);
+            }
+        };
+        // loads per stage of this wave: its panel's W fragments and every
+        // fourth masked-row fragment
+        constexpr int NL_HI = KC * G + (NA + 3) / 4, NL_LO = KC * G + NA / 4;
+        const bool hi = lw < (NA % 4 == 0 ? 4 : NA % 4);
+        auto wait_next = [&](bool more_in_flight) {
+            // the oldest stage in flight has landed once at most the later
+            // stages' loads are outstanding
+            if (!more_in_flight) wait_vmcnt<0>();
+            else if (hi) wait_vmcnt<NL_HI * (NBUF - 2)>();
+            else wait_vmcnt<NL_LO * (NBUF - 2)>();
+        };
+#pragma unroll
+        for (int st = 0; st < NBUF - 1; ++st)
+            if (st < nstage) issue(st);
+        wait_next(NBUF - 1 < nstage && NBUF > 2);
+        __syncthreads();
+        for (int st = 0; st < nstage; ++st) {
+            const bool refill = st + NBUF - 1 < nstage;
+            if (refill) issue(st + NBUF - 1);
+            wait_next(refill && NBUF > 2);
+            __syncthreads();
+        }
+    } else {
+        // ---------------- compute waves ----------------
+        __syncthreads();
+        for (int st = 0; st < nstage; ++st) {
+            const uint8_t* base = ring[st % NBUF] + lane * 16;
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk) {
+                v4u w[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(base + ((wave * KC + kk) * G + g) * 1024);
+#pragma unroll
+                for (int m = 0; m < MSUB; ++m) {
+                    const v4u afr = *(const v4u*)(base + WB + (kk * MSUB + m) * 1024);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        if (BF16) {
+                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(v8bf, afr), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
+                        } else {
+                            const v4f a4 = __builtin_bit_cast(v4f, afr);
+                            const v4f b4 = __builtin_bit_cast(v4f, w[g]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---------------- epilogue (compute waves) ----------------
+        const int grp = lane >> 4, c16 = lane & 15;
+        const int col0 = my_panel * 64 + c16;
+        bool ok[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) ok[g] = active && col0 + 16 * g < P.V;
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * m + 4 * grp + j;
+                const RowMeta mt = s_meta[r];
+                float x[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    x[g] = acc[g][m][j] * mt.scale;
+                    acc[g][m][j] = x[g];
+                }
+                Stat st = stat_empty();
+                if (mt.canon >= 0) {  // not a padding row (the whole 16-lane row agrees)
+                    if (mt.store) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            if (ok[g]) logits[(size_t)mt.canon * P.V + col0 + 16 * g] = x[g];
+                    }
+                    st = row16_stat<G>(x, ok, col0);
+                }
+                if (c16 == 0) s_st[wave][r] = st;
+            }
+        if (tile < P.tiles_lossy) {
+            for (int slot = 0; slot < P.ppg; ++slot) {
+                const int first = slot * P.K;
+                float x[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    // head rows first .. first + K - 1 of this lane group, summed in head order
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int lam = 0; lam < 4 * MSUB; ++lam) {
+                        const int i = lam - first;
+                        if (i >= 0 && i < P.K) {
+                            const float v = acc[g][lam >> 2][lam & 3];
+                            sum = i == 0 ? v : sum + v;
+                        }
+                    }
+                    x[g] = sum * P.inv_k;
+                }
+                const Stat st = row16_stat<G>(x, ok, col0);
+                if (c16 == 0) s_st[wave][ROWS + grp * P.ppg + slot] = st;
+            }
+        }
+    }
+    __syncthreads();
+    // merge the four panels in panel order: part[target][panel group]
+    const int npt = P.GR * P.ppg;
+    const int nloc = ROWS + (tile < P.tiles_lossy ? npt : 0);
+    for (int t = threadIdx.x; t < nloc; t += blockDim.x) {
+        Stat st = s_st[0][t];
+#pragma unroll
+        for (int w = 1; w < CW; ++w) st = stat_merge(st, s_st[w][t]);
+        int target = tile * ROWS + t;
+        if (t >= ROWS) {
+            const int p = tile * npt + (t - ROWS);
+            if (p >= P.n_lossy_pos) continue;
+            target = P.R_phys + p;
+        }
+        part[(size_t)target * P.n_vgroups + group] = st;
     }
 }
 
@@ -1056,8 +1275,32 @@ static hipError_t launch_skinny_t(const Plan& P, const void* W, const void* Hm, 
     return hipGetLastError();
 }
 
+template <bool BF16>
+static hipError_t launch_tile_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
+                                Stat* part, hipStream_t st) {
+    const int n_groups = (P.n_panels + 3) / 4;
+    const int per_xcd = (n_groups + 7) / 8;
+    dim3 grid(8 * per_xcd * P.n_tiles), block(kTileThreads);
+    const uint8_t* w = (const uint8_t*)Wp;
+    const uint8_t* a = (const uint8_t*)Hp;
+    switch (P.msub) {
+        case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 6: hipLaunchKernelGGL((k_gemm_tile<BF16, 6>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const Plan& P, const void* W, const void* Hm, const RowMeta* meta, float* logits, Stat* part,
                        hipStream_t st) {
+    if (P.w_packed && P.tile_kernel)
+        return P.dtype == 1 ? launch_tile_t<true>(P, W, Hm, meta, logits, part, st)
+                            : launch_tile_t<false>(P, W, Hm, meta, logits, part, st);
     if (P.w_packed)
         return P.dtype == 1 ? launch_panel_t<true>(P, W, Hm, meta, logits, part, st)
                             : launch_panel_t<false>(P, W, Hm, meta, logits, part, st);

@@ -118,6 +118,27 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
             best_tiles = tl + tn;
         }
     }
+    // Panel-ordered W with more rows than one small tile holds: the
+    // matrix-core kernel, tiles of 4..10 sub-tiles, the fewest padded rows
+    // (ties: the larger tile, so W is re-read by fewer tiles).
+    P.tile_kernel = 0;
+    if (w_packed && best_tiles > 1) {
+        P.tile_kernel = 1;
+        best_ms = 0;
+        long long best_rows = 0;
+        for (int ms = 4; ms <= 10; ++ms) {
+            const int S = 4 * ms;
+            const int ppg = S / K;
+            const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
+            const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
+            const long long rows = (long long)(tl + tn) * 16 * ms;
+            if (best_ms == 0 || rows <= best_rows) {
+                best_ms = ms;
+                best_rows = rows;
+                best_tiles = tl + tn;
+            }
+        }
+    }
     P.msub = best_ms;
     P.MT = 16 * best_ms;
     P.S = 4 * best_ms;
@@ -130,7 +151,8 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
     P.nkb = (int)((size_t)D.d * elem_size(D.dtype) / 64);
     P.n_panels = cdiv(P.V, 64);
     if (w_packed) {
-        // one wave per (panel, tile); statistic partials per group of four panels
+        // one wave per (panel, tile); statistic partials per group of four
+        // panels (both panel-order kernels)
         P.n_vgroups = cdiv(P.n_panels, 4);
     } else {
         const int nstr = cdiv(P.V, 16);

@@ -63,7 +63,9 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     CHECK((size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) <= sz.part, "part overflow\n");
     CHECK((size_t)P.n_js_pos * P.js_chunks * (K + 1) * sizeof(float) <= sz.jspart || P.n_js_pos == 0,
           "jspart overflow\n");
-    CHECK(P.GR * P.ppg <= 64 && P.MT <= 64 && P.ppg >= 1, "tile shape\n");
+    CHECK(P.GR * P.ppg <= 2 * P.MT && P.ppg >= 1, "tile shape\n");
+    CHECK(P.tile_kernel ? (wp && P.msub >= 4 && P.msub <= 10) : (P.MT <= 64 && P.msub >= 1 && P.msub <= 4),
+          "kernel choice %d msub %d\n", P.tile_kernel, P.msub);
     CHECK(P.n_js_pos == 0 || ((long long)P.js_chunks * P.js_chunk >= V && (long long)(P.js_chunks - 1) * P.js_chunk < V),
           "js chunks\n");
     CHECK(nl == 0 || ((long long)P.race_chunks * P.race_chunk >= V && (long long)(P.race_chunks - 1) * P.race_chunk < V),
