@@ -119,22 +119,25 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         }
     }
     // Panel-ordered W with more rows than one small tile holds: the
-    // matrix-core kernel, tiles of 4..10 sub-tiles, the fewest padded rows
-    // (ties: the larger tile, so W is re-read by fewer tiles).
+    // matrix-core kernel, tiles of 4..10 sub-tiles.  A workgroup computes
+    // MT x 256 outputs from (MT + 256) operand rows per fragment, so the
+    // cost of a choice is its padded rows times (MT + 256) / MT (operand
+    // traffic per output); the cheapest wins, ties going to the larger tile.
     P.tile_kernel = 0;
     if (w_packed && best_tiles > 1) {
         P.tile_kernel = 1;
         best_ms = 0;
-        long long best_rows = 0;
+        double best_cost = 0.0;
         for (int ms = 4; ms <= 10; ++ms) {
             const int S = 4 * ms;
             const int ppg = S / K;
             const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
             const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
-            const long long rows = (long long)(tl + tn) * 16 * ms;
-            if (best_ms == 0 || rows <= best_rows) {
+            const double mt = 16.0 * ms;
+            const double cost = (double)(tl + tn) * mt * (mt + 256.0) / mt;
+            if (best_ms == 0 || cost <= best_cost) {
                 best_ms = ms;
-                best_rows = rows;
+                best_cost = cost;
                 best_tiles = tl + tn;
             }
         }
