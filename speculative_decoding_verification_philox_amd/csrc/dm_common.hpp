@@ -79,14 +79,35 @@ __host__ __device__ inline int rank_of(const uint32_t* bits, int b, bool set) {
     return r + __builtin_popcount(below);
 }
 
+// Position of the k-th (0-based) set bit of x; x has more than k set bits.
+__host__ __device__ inline int select_in_word(uint32_t x, int k) {
+    int pos = 0;
+    for (int w = 16; w >= 1; w >>= 1) {
+        const uint32_t low = x & ((1u << w) - 1u);
+        const int c = __builtin_popcount(low);
+        if (k >= c) {
+            k -= c;
+            x >>= w;
+            pos += w;
+        } else {
+            x = low;
+        }
+    }
+    return pos;
+}
+
 // The sequence index of the `rank`-th member of the set (set bits when `set`,
 // clear bits otherwise) among sequences [0, B); -1 if there is none.
 __host__ __device__ inline int select_of(const uint32_t* bits, int B, int rank, bool set) {
-    for (int b = 0; b < B; ++b) {
-        if (bit_of(bits, b) == set) {
-            if (rank == 0) return b;
-            --rank;
-        }
+    if (rank < 0) return -1;
+    const int nw = (B + 31) >> 5;
+    for (int w = 0; w < nw; ++w) {
+        uint32_t x = set ? bits[w] : ~bits[w];
+        const int valid = B - 32 * w;  // sequences covered by this word
+        if (valid < 32) x &= (1u << valid) - 1u;
+        const int c = __builtin_popcount(x);
+        if (rank < c) return 32 * w + select_in_word(x, rank);
+        rank -= c;
     }
     return -1;
 }

@@ -1,6 +1,7 @@
 // dm_kernels.hip -- HIP kernels of the DropMatch verify step for gfx950.
 //
 //   k_prep        dropout masks from Philox, masked hidden rows in GEMM order
+//                 (k_prep_packed: the same in matrix-core operand order)
 //   k_pack_w      one-time reorder of the LM-head weight into panel order
 //   k_gemm_panel  LM-head GEMM over panel-ordered W: one wave streams one
 //                 panel of 64 vocabulary rows straight into MFMA operands,
@@ -36,10 +37,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // (position, head, element), drawn from Philox stream 0 with counter
 // (j / 4, b * (gamma + 1) + t, i, 0).  The inverted-dropout scale of Eq. (2)
 // is applied to the fp32 accumulator later, so masked values stay exact.
-// Hm is written row-major for the row-major-W kernel, or in matrix-core
-// operand order (per tile: [fragment kb][sub-tile m][lane][16 B], lane
-// 16 a + r holding bytes 64 kb + 16 a .. + 16 of sub-tile row r) for the
-// panel kernel.
+// Hm is written row-major, for the row-major-W kernel.
 // =====================================================================
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restrict__ h, void* __restrict__ Hm,
@@ -80,7 +78,6 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
     const size_t src_row = ri.b >= 0 ? (size_t)(ri.b * P.T1 + ri.t) * P.d : 0;
     const uint8_t* src = (const uint8_t*)h + (src_row + (size_t)e * 8) * esz;
     const size_t row_bytes = (size_t)P.d * esz;
-    const int tile = rho / P.MT, r = rho - tile * P.MT;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         v4u x = ri.b >= 0 ? *(const v4u*)(src + 16 * v) : v4u{0, 0, 0, 0};
@@ -95,14 +92,7 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
             for (int k = 0; k < 4; ++k) x[k] = ((bits >> (4 * v + k)) & 1u) ? x[k] : 0u;
         }
         const size_t o = (size_t)e * 8 * esz + 16 * v;  // byte offset within the row
-        size_t dst;
-        if (P.w_packed) {
-            const size_t frag = ((size_t)tile * P.nkb + (o >> 6)) * P.msub + (r >> 4);
-            dst = frag * 1024 + (size_t)(16 * ((o >> 4) & 3) + (r & 15)) * 16;
-        } else {
-            dst = (size_t)rho * row_bytes + o;
-        }
-        *(v4u*)((uint8_t*)Hm + dst) = x;
+        *(v4u*)((uint8_t*)Hm + (size_t)rho * row_bytes + o) = x;
     }
     if (dbg_mask) {
         // four neighbouring threads hold the 32 bits of one mask word
@@ -111,6 +101,75 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
         word |= __shfl_xor(word, 2, 64);
         if (ri.b >= 0 && (e & 3) == 0) dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * (P.d >> 5) + (e >> 2)] = word;
     }
+}
+
+// =====================================================================
+// k_prep_packed: the same masked rows, written in matrix-core operand order
+// (per tile: [fragment kb][sub-tile m][lane][16 B], lane 16 a + r holding
+// bytes 64 kb + 16 a .. + 16 of sub-tile row r) for the panel-order kernels.
+// One thread per 16-byte piece of the output, so consecutive threads write
+// consecutive bytes; the source row piece is gathered from h (L2-resident).
+// =====================================================================
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* __restrict__ h, void* __restrict__ Hm,
+                                                     RowMeta* __restrict__ meta, uint32_t* __restrict__ dbg_mask) {
+    constexpr int esz = BF16 ? 2 : 4;
+    constexpr int EPP = 16 / esz;  // elements per 16-byte piece
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t n16 = (size_t)P.R_phys * P.nkb * 4;
+    if (q >= n16) return;
+    const int lane = (int)(q & 63);
+    const size_t frag = q >> 6;  // (tile * nkb + kb) * msub + m
+    const int m = (int)(frag % (size_t)P.msub);
+    const size_t tk = frag / (size_t)P.msub;
+    const int kb = (int)(tk % (size_t)P.nkb);
+    const int tile = (int)(tk / (size_t)P.nkb);
+    const int r = 16 * m + (lane & 15);
+    const int rho = tile * P.MT + r;
+    const int o = kb * 64 + (lane >> 4) * 16;  // byte offset within the row
+    const int e0 = o / esz;                   // first element of the piece
+    const RowInfo ri = row_info(P, rho);
+    if (kb == 0 && (lane >> 4) == 0) {
+        RowMeta mt;
+        const bool valid = ri.b >= 0;
+        mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
+        mt.scale = valid ? (ri.lossy ? P.scale : 1.0f) : 0.0f;
+        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
+        mt.pad = 0;
+        meta[rho] = mt;
+    }
+    uint32_t bits = 0u;  // bit k: keep element e0 + k
+    if (ri.b >= 0) {
+        if (ri.lossy) {
+            const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
+#pragma unroll
+            for (int qq = 0; qq < EPP / 4; ++qq) {
+                const u32x4 rr =
+                    philox10(u32x4{(uint32_t)(e0 / 4 + qq), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
+                bits |= (uint32_t)(rr.x >= P.thresh) << (4 * qq);
+                bits |= (uint32_t)(rr.y >= P.thresh) << (4 * qq + 1);
+                bits |= (uint32_t)(rr.z >= P.thresh) << (4 * qq + 2);
+                bits |= (uint32_t)(rr.w >= P.thresh) << (4 * qq + 3);
+            }
+        } else {
+            bits = (1u << EPP) - 1u;
+        }
+    }
+    v4u x = v4u{0, 0, 0, 0};
+    if (ri.b >= 0) x = *(const v4u*)((const uint8_t*)h + ((size_t)(ri.b * P.T1 + ri.t) * P.d) * esz + o);
+    if (BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = (bits >> (2 * k)) & 1u, hi = (bits >> (2 * k + 1)) & 1u;
+            x[k] = (lo ? (x[k] & 0x0000ffffu) : 0u) | (hi ? (x[k] & 0xffff0000u) : 0u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = ((bits >> k) & 1u) ? x[k] : 0u;
+    }
+    *(v4u*)((uint8_t*)Hm + q * 16) = x;
+    if (dbg_mask && ri.b >= 0)  // keep bits of this piece into their mask word (the word starts zeroed)
+        atomicOr(&dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * (P.d >> 5) + (e0 >> 5)], bits << (e0 & 31));
 }
 
 // =====================================================================
@@ -1230,6 +1289,15 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {
 // launch wrappers
 // =====================================================================
 hipError_t launch_prep(const Plan& P, const void* h, void* Hm, RowMeta* meta, uint32_t* dbg_mask, hipStream_t st) {
+    if (P.w_packed) {
+        const size_t n16 = (size_t)P.R_phys * P.nkb * 4;
+        const dim3 grid((unsigned)((n16 + 255) / 256));
+        if (P.dtype == 1)
+            hipLaunchKernelGGL(k_prep_packed<true>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+        else
+            hipLaunchKernelGGL(k_prep_packed<false>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+        return hipGetLastError();
+    }
     const dim3 grid(P.R_phys, ((P.d >> 3) + 255) / 256);
     if (P.dtype == 1)
         hipLaunchKernelGGL(k_prep<true>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);

@@ -116,7 +116,37 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     }
 }
 
+// select_of against a plain scan, for random sets and every rank.
+static void check_select() {
+    unsigned s = 12345u;
+    for (int trial = 0; trial < 2000; ++trial) {
+        uint32_t bits[kMaskWords];
+        for (int w = 0; w < kMaskWords; ++w) {
+            s = s * 1103515245u + 12345u;
+            uint32_t x = s;
+            s = s * 1103515245u + 12345u;
+            x ^= s << 7;
+            if (trial % 5 == 0) x = 0u;
+            if (trial % 7 == 0) x = 0xffffffffu;
+            bits[w] = x;
+        }
+        const int B = 1 + (int)(s % 256u);
+        for (int set = 0; set <= 1; ++set) {
+            int rank = 0;
+            for (int b = 0; b < B; ++b) {
+                if ((int)bit_of(bits, b) == set) {
+                    CHECK(select_of(bits, B, rank, set) == b, "select_of rank %d -> %d, want %d\n", rank,
+                          select_of(bits, B, rank, set), b);
+                    ++rank;
+                }
+            }
+            CHECK(select_of(bits, B, rank, set) == -1, "select_of past the end\n");
+        }
+    }
+}
+
 int main() {
+    check_select();
     int cases = 0;
     const int Ks[] = {1, 2, 3, 4, 5, 7, 8, 13, 16};
     for (int kmax : {5, 8, 16})
