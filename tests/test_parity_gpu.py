@@ -175,3 +175,41 @@ def test_output_histogram_small_vocab_gpu():
         counts += np.bincount(first, minlength=V)
     ver.close()
     assert chi2_pvalue(counts, p) > 1e-3
+
+
+# ------------------------------------------------------------ the limits
+def test_maximum_batch_gamma_and_heads(layout):
+    """max_batch = 256, gamma = 31 (32 positions), K = 16, all three rules;
+    the oracle checks a sample of sequences (a sequence's outputs depend only
+    on its own rows)."""
+    import torch
+
+    w = wl.generate(2, B=256, gamma=31, d=64, V=700, K=16, planted=0.6)
+    modes = (np.arange(256) % 3).astype(np.uint8)
+    ver = P.make_verifier(w.W, w.h, 16)
+    inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
+    seqs = np.array([0, 1, 2, 77, 128, 200, 254, 255], np.int32)
+    for seed in (3, 2**40 + 5):
+        print(f"  B=256 gamma=31 K=16 seed={seed} layout={layout}", flush=True)
+        g = P.run_gpu(ver, inp, modes, 16, 0.3, seed, layout=layout)
+        o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, modes, 16, 0.3, seed, seqs=seqs)
+        P.compare(g, o, modes, 16, seqs=seqs)
+    ver.close()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("V", [1, 2, 63, 65])
+def test_tiny_vocabularies(V, layout):
+    """Fewer entries than one panel (and a single entry): the statistics,
+    JS and race run over partial panels."""
+    w = wl.generate(1, B=6, gamma=3, d=64, V=V, K=3, planted=0.5)
+    modes = np.array([0, 1, 2, 0, 1, 2], np.uint8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, 3, 0.2, [1, 2], layout=layout)
+
+
+@pytest.mark.parametrize("p_drop", [0.0, 0.5, 0.999])
+def test_dropout_extremes(p_drop, layout):
+    """No dropout, half, and nearly everything dropped (scale 1000)."""
+    w = wl.generate(2, B=5, gamma=4, d=256, V=2048, K=5, planted=0.8)
+    modes = np.array([2, 1, 0, 2, 1], np.uint8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, 5, p_drop, [4, 2**33 + 9], layout=layout)
