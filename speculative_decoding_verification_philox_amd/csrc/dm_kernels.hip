@@ -416,30 +416,49 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
 
 // =====================================================================
 // k_gemm_tile: the LM head for many rows (the matrix-core-bound regime):
-// L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] for one tile of
-// 16 * MSUB rows (up to 160) and one group of four panels per workgroup.
+// L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] (DropMatch Eq. (3)
+// with the shared head W).  One workgroup computes one group of four panels
+// (256 vocabulary columns) against a pair of row tiles (2 x 16 * MSUB rows).
 //
-// Warp-specialised: waves 0-3 compute, waves 4-7 load.  The loaders copy
-// each stage (kTileKC fragments of the four panels of W and of the tile's
-// packed Hm) from global memory straight into an LDS ring (direct
-// global-to-LDS loads, 16 bytes per lane, so a fragment is one instruction);
-// the compute waves only read LDS and issue v_mfma_f32_16x16x32_bf16
-// (16x16x4 for fp32), 4 x MSUB per fragment.  One barrier per stage: the
-// loaders have waited for the next stage's loads, the compute waves have
-// finished the stage the loaders refill next.  Blocks are mapped so that
-// the tiles sharing a panel group run together on one XCD (workgroups go to
-// the eight XCDs in turn), where the group's W is read from HBM once and
-// then from that XCD's L2.
+// Eight waves; wave w owns panel w % 4 of the group and tile w / 4 of the
+// pair, so each W fragment in LDS feeds two waves and each masked-row
+// fragment four.  Every wave also loads: a stage is one 64-byte slice of the
+// reduction index (16 W fragments and 2 x MSUB masked-row fragments of
+// 1 KiB), copied from global memory straight into a kTileNBUF-deep LDS ring
+// (direct global-to-LDS loads, 16 bytes per lane, one instruction per
+// fragment, the fragments dealt round-robin to the waves).  Per stage a wave
+// refills the slot freed at the last barrier, multiplies the current slot
+// (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4 for fp32), waits until its
+// own loads of the next stage have landed, and meets the others at one
+// barrier.  The barrier is a bare s_barrier: the workgroup fence of an
+// ordinary barrier would also wait for the loads of the later stages still
+// in flight, which empties the ring every stage.
 //
-// The epilogue is the panel kernel's, with the row metadata in LDS:
-// statistics per row and per centroid over each compute wave's 64 columns,
-// merged across the four into part[target][panel group]; stored rows
-// written.
+// Per multiply-add this fetches a third fewer operand bytes than a 256 x
+// 160 tile; the path from L2 into the CUs is what bounds the loop.  Blocks
+// are mapped so that the tile pairs sharing a panel group run together on
+// one XCD (workgroups go to the eight XCDs in turn), where the group's W is
+// read from HBM once and then from that XCD's L2.
+//
+// The epilogue (in the ring's memory): statistics per row and per centroid
+// over each wave's 64 columns, merged across the four panels into
+// part[target][panel group]; stored rows written.
 // =====================================================================
-constexpr int kTileComputeWaves = 4;
-constexpr int kTileThreads = 2 * kTileComputeWaves * 64;
-constexpr int kTileKC = 2;    // fragments per LDS stage
-constexpr int kTileNBUF = 2;  // stages in the ring
+constexpr int kTileColWaves = 4;  // 64-column panels per workgroup
+constexpr int kTileRowWaves = 2;  // row tiles per workgroup
+constexpr int kTileWaves = kTileColWaves * kTileRowWaves;
+constexpr int kTileThreads = kTileWaves * 64;
+constexpr int kTileNBUF = 4;  // stages in the LDS ring
+
+template <int MSUB>
+struct TileShape {
+    static constexpr int NW = kTileColWaves * 4;     // W fragments per stage
+    static constexpr int NA = kTileRowWaves * MSUB;  // masked-row fragments per stage
+    static constexpr int NF = NW + NA;
+    static constexpr int NJ = (NF + kTileWaves - 1) / kTileWaves;  // most fragments one wave loads per stage
+    static constexpr int STAGE = NF * 1024;
+    static constexpr int LDS = kTileNBUF * STAGE;
+};
 
 #define DM_AS_GLOBAL __attribute__((address_space(1)))
 #define DM_AS_LDS __attribute__((address_space(3)))
@@ -452,31 +471,81 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Barrier between ring stages: this wave's LDS reads are complete
+// (lgkmcnt 0) and its loads of the next stage have landed (waited for by
+// the caller).  The memory clobber keeps the compiler from moving any memory
+// access across it.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
 template <bool BF16, int MSUB>
 __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
                                                             const uint8_t* __restrict__ Hp,
                                                             const RowMeta* __restrict__ meta,
                                                             float* __restrict__ logits,
                                                             Stat* __restrict__ part) {
-    constexpr int ROWS = 16 * MSUB, G = 4, KC = kTileKC, NBUF = kTileNBUF, CW = kTileComputeWaves;
-    constexpr int WB = CW * KC * G * 1024;  // W bytes per stage (four panels)
-    constexpr int AB = KC * MSUB * 1024;    // masked-row bytes per stage
-    constexpr int NA = KC * MSUB;           // masked-row fragments per stage
-    __shared__ __align__(16) uint8_t ring[NBUF][WB + AB];
-    __shared__ Stat s_st[CW][2 * ROWS];
-    __shared__ RowMeta s_meta[ROWS];
+    using TS = TileShape<MSUB>;
+    constexpr int ROWS = 16 * MSUB, G = 4, WC = kTileColWaves, WR = kTileRowWaves, NBUF = kTileNBUF;
+    constexpr int NW = TS::NW, NF = TS::NF, NJ = TS::NJ;
+    constexpr size_t ST_BYTES = (size_t)WR * WC * 2 * ROWS * sizeof(Stat);
+    static_assert(ST_BYTES + WR * ROWS * sizeof(RowMeta) <= (size_t)TS::LDS, "epilogue fits in the ring");
+    static_assert(NJ * (NBUF - 2) < 64, "vmcnt range");
+    __shared__ __align__(16) uint8_t ring[TS::LDS];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_groups = (P.n_panels + 3) >> 2;
+    const int n_pairs = (P.n_tiles + WR - 1) / WR;
     const int per_xcd = (n_groups + 7) >> 3;
     const int xcd = blockIdx.x & 7, k_local = blockIdx.x >> 3;
-    const int group = xcd * per_xcd + k_local / P.n_tiles;
-    const int tile = k_local % P.n_tiles;
+    const int group = xcd * per_xcd + k_local / n_pairs;
+    const int pair = k_local % n_pairs;
     if (group >= n_groups) return;  // the whole block, before any barrier
     const int nkb = P.nkb;
-    const int nstage = nkb / KC;  // nkb is even (d is a multiple of 64)
+    const int wc = wave % WC, wr = wave / WC;
+    const int tile = pair * WR + wr;
+    const bool has_tile = tile < P.n_tiles;  // an odd tile count idles the last pair's second row of waves
+    const int my_panel = group * 4 + wc;
 
-    for (int r = threadIdx.x; r < ROWS; r += blockDim.x) s_meta[r] = meta[(size_t)tile * ROWS + r];
+    // This wave's share of every stage: fragments wave, wave + 8, ... (the
+    // four panels' W first, then both tiles' masked rows).  A missing panel
+    // or tile reads a valid one; its products are never used.
+    const uint8_t* src[NJ];
+    int stride[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int f = wave + kTileWaves * j;
+        if (f < NW) {
+            const int p = min(group * 4 + f / G, P.n_panels - 1);
+            src[j] = Wp + ((size_t)p * nkb * G + f % G) * 1024 + lane * 16;
+            stride[j] = G * 1024;
+        } else {
+            const int fa = f - NW;  // past the last fragment for some waves at j = NJ - 1: never issued
+            const int t = min(pair * WR + fa / MSUB, P.n_tiles - 1);
+            src[j] = Hp + ((size_t)t * nkb * MSUB + fa % MSUB) * 1024 + lane * 16;
+            stride[j] = MSUB * 1024;
+        }
+    }
+    const bool full_share = NF % kTileWaves == 0 || wave < NF % kTileWaves;  // NJ loads per stage, else NJ - 1
+    auto issue = [&](int st) {
+        uint8_t* base = ring + (st % NBUF) * TS::STAGE;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int f = wave + kTileWaves * j;
+            if (f < NF)
+                __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(src[j] + (size_t)st * stride[j]),
+                                                 (DM_AS_LDS void*)(base + f * 1024), 16, 0, 0);
+        }
+    };
+    // the stage after the current one has landed once at most the stages
+    // issued after it are in flight (NBUF - 2 of them after a refill; the
+    // tail waits for everything)
+    auto wait_next = [&](bool refilled) {
+        if (!refilled) wait_vmcnt<0>();
+        else if (full_share) wait_vmcnt<NJ * (NBUF - 2)>();
+        else wait_vmcnt<(NJ - 1) * (NBUF - 2)>();
+    };
 
     v4f acc[G][MSUB];
 #pragma unroll
@@ -484,94 +553,65 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int my_panel = group * 4 + (wave & 3);
-    const bool active = wave < CW && my_panel < P.n_panels;
-
-    if (wave >= CW) {
-        // ---------------- loader waves ----------------
-        const int lw = wave - CW;
-        const int panel = min(group * 4 + lw, P.n_panels - 1);  // a missing panel reads a valid one
-        const uint8_t* wsrc = Wp + (size_t)panel * nkb * G * 1024 + lane * 16;
-        const uint8_t* asrc = Hp + (size_t)tile * nkb * MSUB * 1024 + lane * 16;
-        auto issue = [&](int st) {
-            uint8_t* base = ring[st % NBUF];
 #pragma unroll
-            for (int f = 0; f < KC * G; ++f)
-                __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(wsrc + ((size_t)st * KC * G + f) * 1024),
-                                                 (DM_AS_LDS void*)(base + (lw * KC * G + f) * 1024), 16, 0, 0);
+    for (int st = 0; st < NBUF - 1; ++st)
+        if (st < nkb) issue(st);
+    wait_next(NBUF - 1 < nkb);
+    ring_barrier();
+    for (int st = 0; st < nkb; ++st) {
+        const bool refill = st + NBUF - 1 < nkb;
+        if (refill) issue(st + NBUF - 1);
+        if (has_tile) {
+            const uint8_t* base = ring + (st % NBUF) * TS::STAGE + lane * 16;
+            v4u w[G];
 #pragma unroll
-            for (int j = 0; j < (NA + 3) / 4; ++j) {
-                const int f = lw + 4 * j;
-                if (f < NA)
-                    __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(asrc + ((size_t)st * NA + f) * 1024),
-                                                     (DM_AS_LDS void*)(base + WB + f * 1024), 16, 0, 0);
-            }
-        };
-        // loads per stage of this wave: its panel's W fragments and every
-        // fourth masked-row fragment
-        constexpr int NL_HI = KC * G + (NA + 3) / 4, NL_LO = KC * G + NA / 4;
-        const bool hi = lw < (NA % 4 == 0 ? 4 : NA % 4);
-        auto wait_next = [&](bool more_in_flight) {
-            // the oldest stage in flight has landed once at most the later
-            // stages' loads are outstanding
-            if (!more_in_flight) wait_vmcnt<0>();
-            else if (hi) wait_vmcnt<NL_HI * (NBUF - 2)>();
-            else wait_vmcnt<NL_LO * (NBUF - 2)>();
-        };
+            for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(base + (wc * G + g) * 1024);
 #pragma unroll
-        for (int st = 0; st < NBUF - 1; ++st)
-            if (st < nstage) issue(st);
-        wait_next(NBUF - 1 < nstage && NBUF > 2);
-        __syncthreads();
-        for (int st = 0; st < nstage; ++st) {
-            const bool refill = st + NBUF - 1 < nstage;
-            if (refill) issue(st + NBUF - 1);
-            wait_next(refill && NBUF > 2);
-            __syncthreads();
-        }
-    } else {
-        // ---------------- compute waves ----------------
-        __syncthreads();
-        for (int st = 0; st < nstage; ++st) {
-            const uint8_t* base = ring[st % NBUF] + lane * 16;
+            for (int m = 0; m < MSUB; ++m) {
+                const v4u afr = *(const v4u*)(base + (NW + wr * MSUB + m) * 1024);
 #pragma unroll
-            for (int kk = 0; kk < KC; ++kk) {
-                v4u w[G];
+                for (int g = 0; g < G; ++g) {
+                    if (BF16) {
+                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(v8bf, afr), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
+                    } else {
+                        const v4f a4 = __builtin_bit_cast(v4f, afr);
+                        const v4f b4 = __builtin_bit_cast(v4f, w[g]);
 #pragma unroll
-                for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(base + ((wave * KC + kk) * G + g) * 1024);
-#pragma unroll
-                for (int m = 0; m < MSUB; ++m) {
-                    const v4u afr = *(const v4u*)(base + WB + (kk * MSUB + m) * 1024);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        if (BF16) {
-                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(v8bf, afr), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
-                        } else {
-                            const v4f a4 = __builtin_bit_cast(v4f, afr);
-                            const v4f b4 = __builtin_bit_cast(v4f, w[g]);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
                     }
                 }
             }
-            __syncthreads();
         }
+        wait_next(refill);
+        ring_barrier();
+    }
 
-        // ---------------- epilogue (compute waves) ----------------
+    // ---------------- epilogue (the ring is free: every load has landed) ----------------
+    Stat* s_st = reinterpret_cast<Stat*>(ring);  // [wr][wc][2 * ROWS]
+    RowMeta* s_meta = reinterpret_cast<RowMeta*>(ring + ST_BYTES);  // [wr][ROWS]
+    for (int r = threadIdx.x; r < WR * ROWS; r += blockDim.x) {
+        const int t = pair * WR + r / ROWS;
+        RowMeta mt{-1, 0.0f, 0, 0};
+        if (t < P.n_tiles) mt = meta[(size_t)t * ROWS + r % ROWS];
+        s_meta[r] = mt;
+    }
+    __syncthreads();
+    Stat* my_st = s_st + (size_t)(wr * WC + wc) * 2 * ROWS;
+    if (has_tile) {
+        const RowMeta* my_meta = s_meta + wr * ROWS;
         const int grp = lane >> 4, c16 = lane & 15;
         const int col0 = my_panel * 64 + c16;
         bool ok[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) ok[g] = active && col0 + 16 * g < P.V;
+        for (int g = 0; g < G; ++g) ok[g] = my_panel < P.n_panels && col0 + 16 * g < P.V;
 #pragma unroll
         for (int m = 0; m < MSUB; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * m + 4 * grp + j;
-                const RowMeta mt = s_meta[r];
+                const RowMeta mt = my_meta[r];
                 float x[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
@@ -587,7 +627,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
                     }
                     st = row16_stat<G>(x, ok, col0);
                 }
-                if (c16 == 0) s_st[wave][r] = st;
+                if (c16 == 0) my_st[r] = st;
             }
         if (tile < P.tiles_lossy) {
             for (int slot = 0; slot < P.ppg; ++slot) {
@@ -608,21 +648,26 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
                     x[g] = sum * P.inv_k;
                 }
                 const Stat st = row16_stat<G>(x, ok, col0);
-                if (c16 == 0) s_st[wave][ROWS + grp * P.ppg + slot] = st;
+                if (c16 == 0) my_st[ROWS + grp * P.ppg + slot] = st;
             }
         }
     }
     __syncthreads();
     // merge the four panels in panel order: part[target][panel group]
     const int npt = P.GR * P.ppg;
-    const int nloc = ROWS + (tile < P.tiles_lossy ? npt : 0);
-    for (int t = threadIdx.x; t < nloc; t += blockDim.x) {
-        Stat st = s_st[0][t];
+    for (int u = threadIdx.x; u < WR * 2 * ROWS; u += blockDim.x) {
+        const int rw = u / (2 * ROWS), t = u % (2 * ROWS);
+        const int tl = pair * WR + rw;
+        if (tl >= P.n_tiles) continue;
+        const int nloc = ROWS + (tl < P.tiles_lossy ? npt : 0);
+        if (t >= nloc) continue;
+        const Stat* col = s_st + (size_t)rw * WC * 2 * ROWS + t;
+        Stat st = col[0];
 #pragma unroll
-        for (int w = 1; w < CW; ++w) st = stat_merge(st, s_st[w][t]);
-        int target = tile * ROWS + t;
+        for (int c = 1; c < WC; ++c) st = stat_merge(st, col[(size_t)c * 2 * ROWS]);
+        int target = tl * ROWS + t;
         if (t >= ROWS) {
-            const int p = tile * npt + (t - ROWS);
+            const int p = tl * npt + (t - ROWS);
             if (p >= P.n_lossy_pos) continue;
             target = P.R_phys + p;
         }
@@ -1348,7 +1393,8 @@ static hipError_t launch_tile_t(const Plan& P, const void* Wp, const void* Hp, c
                                 Stat* part, hipStream_t st) {
     const int n_groups = (P.n_panels + 3) / 4;
     const int per_xcd = (n_groups + 7) / 8;
-    dim3 grid(8 * per_xcd * P.n_tiles), block(kTileThreads);
+    const int n_pairs = (P.n_tiles + kTileRowWaves - 1) / kTileRowWaves;
+    dim3 grid(8 * per_xcd * n_pairs), block(kTileThreads);
     const uint8_t* w = (const uint8_t*)Wp;
     const uint8_t* a = (const uint8_t*)Hp;
     switch (P.msub) {
