@@ -68,16 +68,36 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
+def gemm_kernel(cfg, panels: bool, n_lossless: int) -> str:
+    """Which LM-head kernel the library launches: row-major W takes
+    k_gemm_skinny; panel-order W takes k_gemm_panel when the rows fit one
+    small tile (4 lane groups of 4 * ms slots, ms = 1..4, a position's K heads
+    in one group) and k_gemm_tile otherwise."""
+    if not panels:
+        return "k_gemm_skinny"
+    T1 = cfg.gamma + 1
+    lossy_pos, lossless_pos = (cfg.B - n_lossless) * T1, n_lossless * T1
+    best = None
+    for ms in range(1, 5):
+        S = 4 * ms
+        if lossy_pos and S < cfg.K:
+            continue
+        tl = -(-lossy_pos // (4 * (S // cfg.K))) if lossy_pos else 0
+        tn = -(-lossless_pos // (4 * S)) if lossless_pos else 0
+        best = tl + tn if best is None else min(best, tl + tn)
+    return "k_gemm_tile" if best is None or best > 1 else "k_gemm_panel"
+
+
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
-    of this workload, if it was taken on the current kernel source."""
+    of this workload, if it was taken on the current source of that kernel."""
     from speculative_decoding_verification_philox_amd.rocprof_summary import kernel_source_hash
 
     path = os.path.join(PROFILES, f"k_gemm_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel") != kernel or rec.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -232,8 +252,8 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dname]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-    roof["kernel"] = "k_gemm_panel" if w_layout == Bd.DM_W_PANELS else "k_gemm_skinny"
-    roof["traffic"] = measured_traffic(cfg.name)
+    roof["kernel"] = gemm_kernel(cfg, w_layout == Bd.DM_W_PANELS, n_lossless)
+    roof["traffic"] = measured_traffic(cfg.name, roof["kernel"])
 
     cpu = None
     if not args.no_cpu_baseline:

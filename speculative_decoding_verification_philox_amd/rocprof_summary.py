@@ -27,10 +27,29 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(PKG, "csrc", "dm_kernels.hip")
+COMMON_SRC = os.path.join(PKG, "csrc", "dm_common.hpp")
+_HEADER = "// =====================================================================\n// "
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_section(kernel: str) -> str:
+    """The part of the kernel source that defines `kernel`: from its header
+    comment to the next kernel's header."""
+    text = open(KERNEL_SRC).read()
+    start = text.find(_HEADER + kernel + ":")
+    if start < 0:
+        raise KeyError(f"no header comment for {kernel} in {KERNEL_SRC}")
+    end = text.find(_HEADER, start + len(_HEADER))
+    return text[start:end if end >= 0 else len(text)]
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """sha256 (first 16 hex digits) of the whole kernel file, or, for one
+    kernel, of its section plus the shared header it includes."""
+    if kernel is None:
+        data = open(KERNEL_SRC, "rb").read()
+    else:
+        data = (kernel_section(kernel) + open(COMMON_SRC).read()).encode()
+    return hashlib.sha256(data).hexdigest()[:16]
 
 
 def _short(name: str) -> str:
@@ -86,7 +105,8 @@ def traffic(args) -> None:
         "hbm_bytes_per_launch": round(total),
         "algorithmic_bytes_per_launch": args.alg_bytes,
         "traffic_over_algorithmic": round(total / args.alg_bytes, 4) if args.alg_bytes else None,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(args.kernel),
+        "kernel_source_hashed": f"the {args.kernel} section of csrc/dm_kernels.hip plus csrc/dm_common.hpp",
         "command": args.command,
     }
     if args.json:
@@ -108,7 +128,8 @@ def traffic(args) -> None:
     print(f"| algorithmic bytes | {args.alg_bytes:,} |")
     if args.alg_bytes:
         print(f"| traffic / algorithmic | {total / args.alg_bytes:.4f} |")
-    print(f"\nKernel source sha256 (first 16 hex digits): `{kernel_source_hash()}`")
+    print(f"\nSource sha256 (first 16 hex digits) of the `{args.kernel}` section of csrc/dm_kernels.hip plus "
+          f"csrc/dm_common.hpp: `{kernel_source_hash(args.kernel)}`")
 
 
 def main(argv=None) -> None:
