@@ -1035,18 +1035,6 @@ __device__ __forceinline__ unsigned long long u64_max(unsigned long long a, unsi
     return a > b ? a : b;
 }
 
-// Lossy decision at drafted position t of sequence b.
-__device__ __forceinline__ bool lossy_accept(const Plan& P, int b, int t, const int32_t* draft,
-                                             const RowStat* rowstat, bool js, float jq, float jmax) {
-    const int32_t x = draft[b * P.G + t];
-    if (!(x >= 0 && x < P.V)) return false;
-    const int pidx = b * P.T1 + t;
-    int count = 0;
-    for (int i = 0; i < P.K; ++i) count += rowstat[pidx * P.K + i].idx == x;
-    if (!js) return count > 0;             // DropMatch Eq. (4)
-    return jq <= jmax || 2 * count > P.K;  // Algorithm 1: Eq. (6), else Eq. (7)
-}
-
 // Lossless decision at drafted position t: u_t * q(x) < p(x) with p the
 // undropped target distribution and u_t from Philox stream 1.
 __device__ __forceinline__ bool lossless_accept(const Plan& P, int b, int t, const int32_t* draft,
@@ -1241,54 +1229,82 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 // ("Speculative Decoding: Draft, Then Verify", the draft-then-verify loop,
 // steps 3 and 4) and emits one token: the centroid argmax at A for the
 // DropMatch rules, the race winner for lossless sequences (whose race slots
-// it then clears for the next call).  JS sums over the vocabulary chunks
-// are reduced here in a fixed order.
+// it then clears for the next call).
+//
+// The kernel is latency-bound, so it is built around few memory round trips:
+// what the decisions read that does not depend on the JS sums (draft tokens,
+// head and centroid argmaxes, race slots) is fetched first, while groups of
+// four lanes reduce each (position, head-or-draft) JS sum over the
+// vocabulary chunks, sixteen loads in flight per lane, in a fixed order.
 // =====================================================================
-constexpr int kFinishWaves = 4;
-constexpr int kFinishBatch = 4;
-constexpr int kFinishPerLane = 4;  // JS chunks per lane: up to 256 chunks per position
+constexpr int kFinishThreads = 256;
+constexpr int kFinishLanesPerSum = 4;
+constexpr int kFinishLoads = 16;  // JS chunk partials in flight per lane
 
-__global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const Plan P, const int32_t* __restrict__ draft,
-                                               const float* __restrict__ q_hat, const float* __restrict__ logits,
-                                               const RowStat* __restrict__ rowstat,
-                                               const RowStat* __restrict__ centstat,
-                                               const float* __restrict__ jspart,
-                                               unsigned long long* __restrict__ race_best,
-                                               int32_t* __restrict__ accept_len, int32_t* __restrict__ out_token,
-                                               uint8_t* __restrict__ dbg_flags, float* __restrict__ dbg_js_heads,
-                                               float* __restrict__ dbg_js_draft) {
+__global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const int32_t* __restrict__ draft,
+                                                           const float* __restrict__ q_hat,
+                                                           const float* __restrict__ logits,
+                                                           const RowStat* __restrict__ rowstat,
+                                                           const RowStat* __restrict__ centstat,
+                                                           const float* __restrict__ jspart,
+                                                           unsigned long long* __restrict__ race_best,
+                                                           int32_t* __restrict__ accept_len,
+                                                           int32_t* __restrict__ out_token,
+                                                           uint8_t* __restrict__ dbg_flags,
+                                                           float* __restrict__ dbg_js_heads,
+                                                           float* __restrict__ dbg_js_draft) {
     __shared__ float s_js[32][kMaxK + 1];
     const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = P.K, G = P.G, T1 = P.T1;
     const bool lossless = bit_of(P.lossless_bits, b);
     const bool js = bit_of(P.js_bits, b);
+
+    // wave 0, lane t: the inputs of the decision at position t
+    int x = -1, cent_idx = 0;
+    int head_idx[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) head_idx[i] = -1;
+    unsigned long long best_r = 0ull, best_p = 0ull;
+    if (wave == 0) {
+        if (lane < G) x = draft[b * G + lane];
+        if (!lossless) {
+            if (lane <= G) cent_idx = centstat[b * T1 + lane].idx;
+            if (lane < G) {
+#pragma unroll
+                for (int i = 0; i < kMaxK; ++i)
+                    if (i < K) head_idx[i] = rowstat[(b * T1 + lane) * K + i].idx;
+            }
+        } else if (lane == 0) {
+            best_r = race_best[2 * b];
+            best_p = race_best[2 * b + 1];
+        }
+    }
+
     if (js && G > 0) {
-        // wave w sums the (position, head-or-draft) pairs w, w + 4, ... over
-        // the chunks: every load is issued first, then fixed-order sums
-        // (lane-strided, then across the wave)
+        // group g of four lanes sums (position, head-or-draft) pair base + g
+        // over the chunks: lane s of the group takes chunks s, s + 4, ... in
+        // order, then the four partial sums meet in a fixed butterfly
         const int jp0 = rank_of(P.js_bits, b, true) * G;
         const int n_idx = G * (K + 1);
-        for (int base = wave; base < n_idx; base += kFinishWaves * kFinishBatch) {
-            float x[kFinishBatch][kFinishPerLane];
+        const int grp = threadIdx.x / kFinishLanesPerSum, sub = threadIdx.x % kFinishLanesPerSum;
+        constexpr int kGroups = kFinishThreads / kFinishLanesPerSum;
+        for (int base = 0; base < n_idx; base += kGroups) {
+            const int idx = base + grp;
+            const float* src = jspart + ((size_t)jp0 * (K + 1) + min(idx, n_idx - 1)) * P.js_chunks;
+            float acc = 0.0f;
+            for (int c0 = 0; c0 < P.js_chunks; c0 += kFinishLanesPerSum * kFinishLoads) {
+                float v[kFinishLoads];
 #pragma unroll
-            for (int u = 0; u < kFinishBatch; ++u) {
-                const int idx = base + u * kFinishWaves;
-                const float* src = jspart + ((size_t)jp0 * (K + 1) + idx) * P.js_chunks;
-#pragma unroll
-                for (int q = 0; q < kFinishPerLane; ++q) {
-                    const int cc = lane + 64 * q;
-                    x[u][q] = (idx < n_idx && cc < P.js_chunks) ? src[cc] : 0.0f;
+                for (int q = 0; q < kFinishLoads; ++q) {
+                    const int cc = c0 + sub + kFinishLanesPerSum * q;
+                    v[q] = (idx < n_idx && cc < P.js_chunks) ? src[cc] : 0.0f;
                 }
-            }
 #pragma unroll
-            for (int u = 0; u < kFinishBatch; ++u) {
-                const int idx = base + u * kFinishWaves;
-                float acc = x[u][0];
-#pragma unroll
-                for (int q = 1; q < kFinishPerLane; ++q) acc += x[u][q];
-                const float tot = wave_sum(acc);
-                if (lane == 0 && idx < n_idx) s_js[idx / (K + 1)][idx % (K + 1)] = tot;
+                for (int q = 0; q < kFinishLoads; ++q) acc += v[q];
             }
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            if (sub == 0 && idx < n_idx) s_js[idx / (K + 1)][idx % (K + 1)] = acc;
         }
     }
     __syncthreads();
@@ -1297,30 +1313,36 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const Plan P, cons
     if (lane < G) {
         if (lossless) {
             accept = lossless_accept(P, b, lane, draft, q_hat, logits, rowstat);
-        } else if (js) {
-            float jmax = -INFINITY;
-            for (int i = 0; i < K; ++i) jmax = fmaxf(jmax, s_js[lane][i]);
-            const float jq = s_js[lane][K];
-            accept = lossy_accept(P, b, lane, draft, rowstat, true, jq, jmax);
-            if (dbg_js_draft) dbg_js_draft[b * G + lane] = jq;
-            if (dbg_js_heads)
-                for (int i = 0; i < K; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
         } else {
-            accept = lossy_accept(P, b, lane, draft, rowstat, false, 0.0f, 0.0f);
+            int count = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxK; ++i) count += (i < K && head_idx[i] == x) ? 1 : 0;
+            const bool valid = x >= 0 && x < P.V;
+            if (js) {
+                float jmax = -INFINITY;
+                for (int i = 0; i < K; ++i) jmax = fmaxf(jmax, s_js[lane][i]);
+                const float jq = s_js[lane][K];
+                accept = valid && (jq <= jmax || 2 * count > K);  // Algorithm 1: Eq. (6), else Eq. (7)
+                if (dbg_js_draft) dbg_js_draft[b * G + lane] = jq;
+                if (dbg_js_heads)
+                    for (int i = 0; i < K; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
+            } else {
+                accept = valid && count > 0;  // DropMatch Eq. (4)
+            }
         }
         if (dbg_flags) dbg_flags[b * G + lane] = accept ? 1 : 0;
     }
     const int A = first_reject(lane < G && !accept, G);
+    const int token_lossy = __shfl(cent_idx, A, 64);  // greedy on the centroid at A
     if (lane == 0) {
         accept_len[b] = A;
         if (lossless) {
-            unsigned long long best = race_best[2 * b];
-            if (!best) best = race_best[2 * b + 1];
+            const unsigned long long best = best_r ? best_r : best_p;
             out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
             race_best[2 * b] = 0ull;
             race_best[2 * b + 1] = 0ull;
         } else {
-            out_token[b] = centstat[b * T1 + A].idx;  // greedy on the centroid at A
+            out_token[b] = token_lossy;
         }
     }
 }
@@ -1442,7 +1464,7 @@ hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat,
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishWaves * 64), 0, st, P, draft, q_hat, logits, rowstat, centstat,
+    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishThreads), 0, st, P, draft, q_hat, logits, rowstat, centstat,
                        jspart,
                        race_best, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
