@@ -36,7 +36,8 @@ class _Problem(ctypes.Structure):
         ("p_drop", ctypes.c_float), ("pad0", ctypes.c_uint32), ("seed", ctypes.c_uint64),
         ("W", ctypes.c_void_p), ("h", ctypes.c_void_p), ("draft", _c_i32p),
         ("q_hat", _c_f32p), ("modes", _c_u8p), ("n_seq", ctypes.c_int32),
-        ("n_threads", ctypes.c_int32), ("seq", _c_i32p),
+        ("n_threads", ctypes.c_int32), ("seq", _c_i32p), ("temperature", ctypes.c_float),
+        ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("pad1", ctypes.c_uint32),
     ]
 
 
@@ -47,7 +48,8 @@ class _Result(ctypes.Structure):
         ("head_gap", _c_f64p), ("head_max", _c_f64p), ("head_logz", _c_f64p),
         ("centroid_argmax", _c_i32p), ("centroid_gap", _c_f64p), ("centroid_logz", _c_f64p),
         ("js_heads", _c_f64p), ("js_draft", _c_f64p), ("logits", _c_f64p),
-        ("mask_bits", _c_u32p), ("race_gap", _c_f64p),
+        ("mask_bits", _c_u32p), ("race_gap", _c_f64p), ("filter_count", _c_i32p),
+        ("filter_logz", _c_f64p), ("filter_margin", _c_f64p),
     ]
 
 
@@ -89,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.dmo_rule_js.restype = ctypes.c_int
         L.dmo_rule_lossless.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
         L.dmo_rule_lossless.restype = ctypes.c_int
+        L.dmo_processed.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f64p, _c_f64p,
+                                    _c_f64p]
+        L.dmo_processed.restype = ctypes.c_int
         L.dmo_run.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Result)]
         L.dmo_run.restype = ctypes.c_int
         _lib = L
@@ -158,15 +163,29 @@ def rule_lossless(u, px, qx) -> bool:
     return bool(lib().dmo_rule_lossless(float(u), float(px), float(qx)))
 
 
+def processed(l, top_k=0, top_p=0.0):
+    """The processed distribution of one (already tempered) logit row:
+    (p, |S|, log sum_S e^l, margin); see dmo_processed."""
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    p = np.zeros_like(l)
+    lz, mg = ctypes.c_double(), ctypes.c_double()
+    cnt = lib().dmo_processed(_ptr(l, _c_f64p), l.size, int(top_k), float(top_p), _ptr(p, _c_f64p),
+                              ctypes.byref(lz), ctypes.byref(mg))
+    if cnt < 0:
+        raise MemoryError("dmo_processed")
+    return p, int(cnt), lz.value, mg.value
+
+
 # -------------------------------------------------------------- full verify
 def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False,
-        want_masks=False, n_threads=None):
+        want_masks=False, n_threads=None, temperature=0.0, top_k=0, top_p=0.0):
     """Run the verify step for the listed sequences (all by default).
 
     W: [V, d], h: [B, gamma+1, d] (float32 or uint16 bf16 bits, same dtype);
     draft: int32 [B, gamma]; q_hat: float32 [B, gamma, V] or None;
-    modes: uint8 [B].  Returns a dict of numpy arrays whose leading dimension
-    indexes the listed sequences.
+    modes: uint8 [B].  temperature (0 read as 1) divides every logit row;
+    top_k / top_p (0 = off) process the lossless target.  Returns a dict of
+    numpy arrays whose leading dimension indexes the listed sequences.
     """
     W = np.ascontiguousarray(W)
     h = np.ascontiguousarray(h)
@@ -209,6 +228,9 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
         "js_heads": np.full((n, G, K), np.nan),
         "js_draft": np.full((n, G), np.nan),
         "race_gap": np.full(n, np.nan),
+        "filter_count": np.full((n, T1), -1, np.int32),
+        "filter_logz": np.full((n, T1), np.nan),
+        "filter_margin": np.full((n, T1), np.nan),
     }
     if want_logits:
         out["logits"] = np.full((n, T1, K, V), np.nan)
@@ -220,7 +242,8 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
     prob = _Problem(d=d, vocab=V, batch=B, gamma=G, K=K, dtype=dtype, p_drop=float(p_drop), pad0=0,
                     seed=int(seed) & (2**64 - 1), W=W.ctypes.data, h=h.ctypes.data,
                     draft=_ptr(draft, _c_i32p), q_hat=_ptr(q_hat, _c_f32p), modes=_ptr(modes, _c_u8p),
-                    n_seq=n, n_threads=int(n_threads), seq=_ptr(seq, _c_i32p))
+                    n_seq=n, n_threads=int(n_threads), seq=_ptr(seq, _c_i32p),
+                    temperature=float(temperature), top_k=int(top_k), top_p=float(top_p), pad1=0)
     res = _Result(**{name: _ptr(out.get(name), ctype) for name, ctype in _Result._fields_})
     rc = lib().dmo_run(ctypes.byref(prob), ctypes.byref(res))
     if rc != 0:

@@ -193,6 +193,89 @@ int32_t dmo_race(const double* w, int n, uint64_t seed, uint32_t pidx, double* g
 }
 
 /* ------------------------------------------------------------------------ */
+/* The processed target distribution.  [PB] Sec. 1: p and q must already     */
+/* include temperature, top-k, top-p and the renormalisation; [SD]           */
+/* "Production gotchas", "The same sampling settings": the test and the      */
+/* residual use the processed p.  Temperature divides the logits before      */
+/* this step (see dmo_run).  The pages name top-k and top-p without defining */
+/* ties; the readings taken here:                                            */
+/*   top-k (0 < k < n): keep every v whose logit is >= the k-th largest      */
+/*     logit (ties at the boundary are all kept);                            */
+/*   then renormalise over that set S_k;                                     */
+/*   top-p (0 < top_p < 1): keep v in S_k iff the renormalised mass of the   */
+/*     tokens of S_k with a strictly larger logit is below top_p (the        */
+/*     nucleus: the smallest prefix, by probability, whose mass reaches      */
+/*     top_p, with the boundary's ties kept);                                */
+/*   then renormalise over the kept set S.                                   */
+/* k = 0 or >= n, and top_p = 0 or >= 1, switch the filter off.              */
+/* Writes p_out (0 off S), returns |S|; *logz_out = log sum_{v in S} e^l_v,  */
+/* *margin_out = distance of the decisions from flipping: the smallest of    */
+/* the logit gap at the k-th value and the mass gap (relative to S_k's mass) */
+/* at the top_p boundary.                                                    */
+/* ------------------------------------------------------------------------ */
+static const double* g_sort_key;
+static int cmp_desc(const void* a, const void* b)
+{
+    double x = g_sort_key[*(const int32_t*)a], y = g_sort_key[*(const int32_t*)b];
+    if (x > y) return -1;
+    if (x < y) return 1;
+    return (*(const int32_t*)a > *(const int32_t*)b) - (*(const int32_t*)a < *(const int32_t*)b);
+}
+
+int dmo_processed(const double* l, int n, int top_k, double top_p, double* p_out, double* logz_out,
+                  double* margin_out)
+{
+    int32_t* ord = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    if (!ord) return -1;
+    for (int v = 0; v < n; ++v) ord[v] = v;
+    g_sort_key = l; /* the oracle is single-threaded here */
+    qsort(ord, (size_t)n, sizeof(int32_t), cmp_desc);
+    const double m = l[ord[0]];
+    double margin = INFINITY;
+
+    /* top-k: S_k = the first n_k entries of the order, ties at the k-th kept */
+    int n_k = n;
+    if (top_k > 0 && top_k < n) {
+        const double lk = l[ord[top_k - 1]];
+        n_k = top_k;
+        while (n_k < n && l[ord[n_k]] == lk) ++n_k;
+        if (n_k < n) margin = lk - l[ord[n_k]];
+    }
+    double z_k = 0.0;
+    for (int r = 0; r < n_k; ++r) z_k += exp(l[ord[r]] - m);
+
+    /* top-p over the renormalised S_k, walking groups of equal logits */
+    int n_s = n_k;
+    if (top_p > 0.0 && top_p < 1.0) {
+        const double target = top_p * z_k;
+        double above = 0.0; /* mass of S_k strictly above the current group */
+        int r = 0;
+        n_s = 0;
+        while (r < n_k) {
+            int e = r;
+            double group = 0.0;
+            while (e < n_k && l[ord[e]] == l[ord[r]]) group += exp(l[ord[e++]] - m);
+            if (!(above < target)) {
+                margin = fmin(margin, (above - target) / z_k);
+                break;
+            }
+            margin = fmin(margin, (target - above) / z_k);
+            n_s = e;
+            above += group;
+            r = e;
+        }
+    }
+    double z = 0.0;
+    for (int r = 0; r < n_s; ++r) z += exp(l[ord[r]] - m);
+    for (int v = 0; v < n; ++v) p_out[v] = 0.0;
+    for (int r = 0; r < n_s; ++r) p_out[ord[r]] = exp(l[ord[r]] - m) / z;
+    if (logz_out) *logz_out = m + log(z);
+    if (margin_out) *margin_out = margin;
+    free(ord);
+    return n_s;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The three acceptance rules, each on already-reduced quantities.           */
 /* ------------------------------------------------------------------------ */
 
@@ -243,6 +326,10 @@ typedef struct dmo_problem {
     int32_t n_seq;         /* number of sequences evaluated */
     int32_t n_threads;
     const int32_t* seq;    /* [n_seq] batch indices evaluated */
+    float temperature;     /* > 0 divides every logit row; 0 is read as 1 */
+    int32_t top_k;         /* lossless rows; 0 = off */
+    float top_p;           /* lossless rows; 0 or >= 1 = off */
+    uint32_t pad1;
 } dmo_problem;
 
 typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wanted */
@@ -263,6 +350,9 @@ typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wa
     double* logits;           /* [n, gamma+1, K, vocab] */
     uint32_t* mask_bits;      /* [n, gamma+1, K, d/32] */
     double* race_gap;         /* [n] */
+    int32_t* filter_count;    /* [n, gamma+1] lossless sequences: |S| of the processed target */
+    double* filter_logz;      /* [n, gamma+1] lossless sequences: log sum over S of e^l */
+    double* filter_margin;    /* [n, gamma+1] lossless sequences: see dmo_processed */
 } dmo_result;
 
 /* ------------------------------------------------------------------------ */
@@ -273,6 +363,9 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
     const int d = P->d, V = P->vocab, G = P->gamma, K = P->K, T1 = G + 1;
     if (d <= 0 || V <= 0 || G < 0 || K <= 0 || P->batch <= 0) return 1;
     if (!(P->p_drop >= 0.0f && P->p_drop < 1.0f)) return 1;
+    if (!(P->temperature >= 0.0f) || !(P->top_p >= 0.0f) || P->top_k < 0) return 1;
+    /* temperature: the sampled distribution is softmax(l / T) ([PB] Sec. 1) */
+    const double temp = P->temperature > 0.0f ? (double)P->temperature : 1.0;
     const uint32_t thresh = dmo_threshold(P->p_drop);
     const double pd = (double)P->p_drop;
     const int nthreads = P->n_threads > 0 ? P->n_threads : 1;
@@ -281,8 +374,9 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
     double* L = (double*)malloc(sizeof(double) * (size_t)T1 * K * V);
     double* Lbar = (double*)malloc(sizeof(double) * (size_t)T1 * V);
     double* prob = (double*)malloc(sizeof(double) * (size_t)(K + 2) * V);
-    if (!hm || !L || !Lbar || !prob) {
-        free(hm); free(L); free(Lbar); free(prob);
+    double* pproc = (double*)malloc(sizeof(double) * (size_t)T1 * V); /* lossless: processed p per position */
+    if (!hm || !L || !Lbar || !prob || !pproc) {
+        free(hm); free(L); free(Lbar); free(prob); free(pproc);
         return 4;
     }
     double* rmax = (double*)malloc(sizeof(double) * (size_t)T1 * K);
@@ -334,7 +428,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                         const double* x = hm + ((size_t)t * K + i) * d;
                         double s = 0.0;
                         for (int j = 0; j < d; ++j) s += wrow[j] * x[j];
-                        L[((size_t)t * K + i) * V + v] = scale * s;
+                        L[((size_t)t * K + i) * V + v] = scale * s / temp;
                     }
                 }
             }
@@ -354,6 +448,23 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 lb[v] = s / rows;
             }
             dmo_row_stats(lb, V, NULL, &clogz[t], &carg[t], &cgap[t]);
+        }
+
+        /* Lossless sequences: the processed target at every position. */
+        if (!lossy) {
+            for (int t = 0; t < T1; ++t) {
+                double lz, mg;
+                int cnt = dmo_processed(L + ((size_t)t * K) * V, V, P->top_k, (double)P->top_p,
+                                        pproc + (size_t)t * V, &lz, &mg);
+                if (cnt < 0) {
+                    free(hm); free(L); free(Lbar); free(prob); free(pproc);
+                    free(rmax); free(rlogz); free(rgap); free(rarg); free(clogz); free(cgap); free(carg); free(acc);
+                    return 4;
+                }
+                if (R->filter_count) R->filter_count[(size_t)n * T1 + t] = cnt;
+                if (R->filter_logz) R->filter_logz[(size_t)n * T1 + t] = lz;
+                if (R->filter_margin) R->filter_margin[(size_t)n * T1 + t] = mg;
+            }
         }
 
         /* Decisions for every drafted position t < gamma. */
@@ -397,11 +508,12 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 else
                     margin = fmin(m_js, min_gap);
             } else {
-                /* [PB] Sec. 2: the classical test on the undropped target p. */
+                /* [PB] Sec. 2: the classical test on the undropped, processed
+                 * target p. */
                 double u = dmo_accept_uniform(P->seed, pidx);
                 if (R->uniforms) R->uniforms[(size_t)n * G + t] = u;
                 if (valid) {
-                    double px = exp(L[((size_t)t * K) * V + x] - rlogz[t * K]);
+                    double px = pproc[(size_t)t * V + x];
                     double qx = (double)P->q_hat[((size_t)b * G + t) * V + x];
                     accept = dmo_rule_lossless(u, px, qx);
                     margin = qx > 0.0 ? fabs(u - px / qx) : px;
@@ -434,10 +546,10 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
              * the bonus p_gamma when every draft survived; a zero residual
              * (only possible by rounding) falls back to p_A ([PB] Sec. 2). */
             double* w = prob;
-            const double* l = L + ((size_t)A * K) * V;
+            const double* pa = pproc + (size_t)A * V;
             double total = 0.0;
             for (int v = 0; v < V; ++v) {
-                double p = exp(l[v] - rlogz[A * K]);
+                double p = pa[v];
                 if (A < G) {
                     double q = (double)P->q_hat[((size_t)b * G + A) * V + v];
                     w[v] = p - q > 0.0 ? p - q : 0.0;
@@ -447,7 +559,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 total += w[v];
             }
             if (!(total > 0.0))
-                for (int v = 0; v < V; ++v) w[v] = exp(l[v] - rlogz[A * K]);
+                for (int v = 0; v < V; ++v) w[v] = pa[v];
             y = dmo_race(w, V, P->seed, (uint32_t)(b * T1 + A), &race_gap);
         }
 
@@ -471,7 +583,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         }
     }
 
-    free(hm); free(L); free(Lbar); free(prob);
+    free(hm); free(L); free(Lbar); free(prob); free(pproc);
     free(rmax); free(rlogz); free(rgap); free(rarg);
     free(clogz); free(cgap); free(carg); free(acc);
     return 0;
