@@ -147,6 +147,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--p-drop", type=float, default=None)
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="sampling temperature of the target (every rule)")
+    ap.add_argument("--top-k", type=int, default=0, help="top-k of the lossless target (0 = off)")
+    ap.add_argument("--top-p", type=float, default=1.0, help="top-p of the lossless target (1 = off)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w-layout", choices=("panels", "rowmajor"), default="panels",
@@ -208,7 +212,7 @@ def main():
 
     def step():
         ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=stream.cuda_stream, outputs=outs,
-                w_layout=w_layout)
+                w_layout=w_layout, temperature=args.temperature, top_k=args.top_k, top_p=args.top_p)
 
     for _ in range(args.warmup):
         step()
@@ -278,7 +282,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={cfg.B}, gamma={cfg.gamma}, d={cfg.d}, |V|={cfg.V}, K={cfg.K}, "
                                f"p_drop={cfg.p_drop}, {modes_desc}",
-                   "batch": cfg.B, "positions_per_step": positions, "gemm_rows": rows, "w_layout": args.w_layout},
+                   "batch": cfg.B, "positions_per_step": positions, "gemm_rows": rows, "w_layout": args.w_layout,
+                   "sampling": {"temperature": args.temperature, "top_k": args.top_k, "top_p": args.top_p}},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -108,6 +108,19 @@ typedef struct dm_verify_args {
     float p_drop;           /* dropout probability, 0 <= p_drop < 1 */
     uint32_t w_layout;      /* dm_w_layout of W */
     uint64_t seed;          /* Philox key */
+    /* Sampling settings of the target.  The lossless test and its residual
+     * must use the distribution the sampler actually draws from: temperature,
+     * top-k, top-p and the renormalisation ("Why speculative decoding
+     * preserves distributions but may not be faster", Sec. 1; "Speculative
+     * Decoding: Draft, Then Verify", "The same sampling settings").  q_hat is
+     * the draft's processed distribution, used as given.  All three zero =
+     * the plain softmax. */
+    float temperature;      /* > 0 divides every logit row, all rules; 0 is read as 1 */
+    int32_t top_k;          /* LOSSLESS: keep the tokens whose logit is >= the top_k-th largest
+                               (ties kept); 0 or >= vocab = off */
+    float top_p;            /* LOSSLESS: of those, keep the tokens whose strictly larger
+                               renormalised mass is < top_p; 0 or >= 1 = off */
+    uint32_t reserved;      /* 0 */
     int32_t* accept_len;    /* device out [B]: A, drafts accepted before the first rejection */
     int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
     /* Optional device outputs for inspection; NULL = not written. */
@@ -121,6 +134,9 @@ typedef struct dm_verify_args {
     float* logits;             /* [B, gamma+1, K, vocab] every row, fp32 (lossless: head 0) */
     uint32_t* mask_bits;       /* [B, gamma+1, K, d/32] keep bits, bit j%32 of word j/32
                                   (lossless: all ones in head 0) */
+    int32_t* filter_count;     /* [B, gamma+1] LOSSLESS sequences, when top_k or top_p is on:
+                                  size of the kept set */
+    float* filter_logz;        /* [B, gamma+1] same: log of the sum of e^l over the kept set */
 } dm_verify_args;
 
 typedef struct dm_verify dm_verify_t; /* opaque */

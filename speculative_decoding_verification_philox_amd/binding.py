@@ -39,11 +39,13 @@ class dm_verify_args(ctypes.Structure):
     _fields_ = [
         ("W", ctypes.c_void_p), ("h", ctypes.c_void_p), ("draft", ctypes.c_void_p), ("q_hat", ctypes.c_void_p),
         ("modes", ctypes.c_void_p), ("batch", ctypes.c_int32), ("K", ctypes.c_int32), ("p_drop", ctypes.c_float),
-        ("w_layout", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("accept_len", ctypes.c_void_p),
+        ("w_layout", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("temperature", ctypes.c_float),
+        ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("reserved", ctypes.c_uint32),
+        ("accept_len", ctypes.c_void_p),
         ("out_token", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
         ("centroid_argmax", ctypes.c_void_p), ("head_logz", ctypes.c_void_p), ("centroid_logz", ctypes.c_void_p),
         ("js_heads", ctypes.c_void_p), ("js_draft", ctypes.c_void_p), ("logits", ctypes.c_void_p),
-        ("mask_bits", ctypes.c_void_p),
+        ("mask_bits", ctypes.c_void_p), ("filter_count", ctypes.c_void_p), ("filter_logz", ctypes.c_void_p),
     ]
 
 
@@ -135,7 +137,7 @@ def dm_verify_destroy(handle: ctypes.c_void_p) -> None:
 
 # ------------------------------------------------------- tensor front end
 DEBUG_OUTPUTS = ("accept_flags", "head_argmax", "centroid_argmax", "head_logz", "centroid_logz", "js_heads",
-                 "js_draft", "logits", "mask_bits")
+                 "js_draft", "logits", "mask_bits", "filter_count", "filter_logz")
 
 
 class Verifier:
@@ -190,7 +192,7 @@ class Verifier:
         return t.data_ptr()
 
     def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, w_layout=DM_W_ROW_MAJOR,
-                  **debug):
+                  temperature=1.0, top_k=0, top_p=1.0, **debug):
         import torch
 
         D = self.desc
@@ -221,13 +223,15 @@ class Verifier:
         a.modes = modes_np.ctypes.data
         a.batch, a.K, a.p_drop = B, int(K), float(p_drop)
         a.seed = int(seed) & (2**64 - 1)
+        a.temperature, a.top_k, a.top_p = float(temperature), int(top_k), float(top_p)
         a.accept_len = self._expect("accept_len", accept_len, (B,), torch.int32, dev)
         a.out_token = self._expect("out_token", out_token, (B,), torch.int32, dev)
         shapes = {"accept_flags": ((B, G), torch.uint8), "head_argmax": ((B, T1, K), torch.int32),
                   "centroid_argmax": ((B, T1), torch.int32), "head_logz": ((B, T1, K), torch.float32),
                   "centroid_logz": ((B, T1), torch.float32), "js_heads": ((B, G, K), torch.float32),
                   "js_draft": ((B, G), torch.float32), "logits": ((B, T1, K, V), torch.float32),
-                  "mask_bits": ((B, T1, K, d // 32), torch.int32)}
+                  "mask_bits": ((B, T1, K, d // 32), torch.int32), "filter_count": ((B, T1), torch.int32),
+                  "filter_logz": ((B, T1), torch.float32)}
         for name, t in debug.items():
             if name not in shapes:
                 raise KeyError(name)
@@ -238,13 +242,15 @@ class Verifier:
         return a
 
     def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None,
-            w_layout=DM_W_ROW_MAJOR):
+            w_layout=DM_W_ROW_MAJOR, temperature=1.0, top_k=0, top_p=1.0):
         """Enqueue one verify step on `stream` (default: torch's current stream).
 
         W is row-major [vocab, d] (w_layout=DM_W_ROW_MAJOR) or the uint8
-        buffer pack_w returns (w_layout=DM_W_PANELS).  Returns a dict with
-        accept_len and out_token (and every debug output when debug=True).
-        Preallocated outputs can be passed in `outputs`."""
+        buffer pack_w returns (w_layout=DM_W_PANELS).  temperature divides
+        every logit row; top_k / top_p (0 / 1 = off) process the lossless
+        target.  Returns a dict with accept_len and out_token (and every debug
+        output when debug=True).  Preallocated outputs can be passed in
+        `outputs`."""
         import torch
 
         D = self.desc
@@ -265,9 +271,11 @@ class Verifier:
             out.setdefault("logits", torch.full((B, T1, K, V), float("nan"), dtype=torch.float32, device=dev))
             if D.d % 32 == 0:
                 out.setdefault("mask_bits", torch.empty((B, T1, K, D.d // 32), dtype=torch.int32, device=dev))
+            out.setdefault("filter_count", torch.full((B, T1), -1, dtype=torch.int32, device=dev))
+            out.setdefault("filter_logz", torch.full((B, T1), float("nan"), dtype=torch.float32, device=dev))
         dbg = {k: v for k, v in out.items() if k in DEBUG_OUTPUTS}
         args = self.make_args(W, h, draft, q_hat, modes, K, p_drop, seed, out["accept_len"], out["out_token"],
-                              w_layout=w_layout, **dbg)
+                              w_layout=w_layout, temperature=temperature, top_k=top_k, top_p=top_p, **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         dm_verify_run(self.handle, args, stream)

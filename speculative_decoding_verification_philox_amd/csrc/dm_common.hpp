@@ -32,7 +32,7 @@ struct Plan {
     // problem
     int B, T1, G, K, V, d;
     int dtype;           // 0 f32, 1 bf16
-    float scale;         // 1 / (1 - p_drop)
+    float scale;         // 1 / ((1 - p_drop) temperature), the dropout rows
     float inv_k;         // 1 / K, the centroid's mean weight
     uint32_t thresh;     // keep iff Philox word >= thresh
     uint32_t key0, key1; // Philox key (seed low, high)
@@ -40,6 +40,11 @@ struct Plan {
     uint32_t lossless_bits[kMaskWords];
     uint32_t js_bits[kMaskWords];
     int n_lossy_seq, n_lossless_seq, n_js_seq;
+    // sampling settings: row scales include 1 / temperature; the filter
+    // (top-k, top-p) applies to lossless rows when `filter` is set
+    float scale_undropped;
+    int filter, top_k;
+    float top_p;
     // slot layout
     int geom, msub, MT, GR, S;
     int ppg;                // lossy positions per group (S / K)
@@ -131,7 +136,7 @@ __host__ __device__ inline void tile_slot(int geom, int r, int* g, int* lambda) 
 // Per physical GEMM row, written by k_prep for the LM-head epilogue.
 struct RowMeta {
     int canon;    // (b * T1 + t) * K + i, or -1 for a padding row
-    float scale;  // 1 / (1 - p_drop) for a dropout row, 1 undropped, 0 padding
+    float scale;  // 1 / ((1 - p_drop) T) for a dropout row, 1 / T undropped, 0 padding
     int store;    // 1 if the row's logits are kept for the vocabulary pass
     int pad;
 };
@@ -263,6 +268,15 @@ struct RowStat {
     float m;
     float logz;
     int idx;
+};
+
+// The processed target of one lossless position: v is kept iff its logit is
+// >= thresh; logz = log of the sum of e^l over the kept tokens.
+struct FiltStat {
+    float thresh;
+    float logz;
+    int count;
+    int pad;
 };
 
 // Mean of the K head logits of one position: the DropMatch centroid logit,

@@ -13,6 +13,8 @@
 //                 workgroup; W streamed from HBM straight into MFMA operands),
 //                 same epilogue
 //   k_combine     merges the per-vocabulary-group statistics
+//   k_filter      top-k / top-p thresholds of the lossless targets (only when
+//                 a filter is set)
 //   k_vocab       Jensen-Shannon terms and the residual race over the
 //                 vocabulary
 //   k_finish      acceptance rule per drafted position, first-rejection
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
         RowMeta mt;
         const bool valid = ri.b >= 0;
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
-        mt.scale = valid ? (ri.lossy ? P.scale : 1.0f) : 0.0f;
+        mt.scale = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
         mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
         mt.pad = 0;
         meta[rho] = mt;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
         RowMeta mt;
         const bool valid = ri.b >= 0;
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
-        mt.scale = valid ? (ri.lossy ? P.scale : 1.0f) : 0.0f;
+        mt.scale = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
         mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
         mt.pad = 0;
         meta[rho] = mt;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
     if (threadIdx.x < ROWS) {
         RowInfo ri = row_info(P, tile * ROWS + threadIdx.x);
         bool valid = ri.b >= 0;
-        s_scale[threadIdx.x] = valid ? (ri.lossy ? P.scale : 1.0f) : 0.0f;
+        s_scale[threadIdx.x] = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
         s_canon[threadIdx.x] = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
         s_store[threadIdx.x] =
             valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
@@ -1039,11 +1041,19 @@ __device__ __forceinline__ unsigned long long u64_max(unsigned long long a, unsi
 // undropped target distribution and u_t from Philox stream 1.
 __device__ __forceinline__ bool lossless_accept(const Plan& P, int b, int t, const int32_t* draft,
                                                 const float* q_hat, const float* logits,
-                                                const RowStat* rowstat) {
+                                                const RowStat* rowstat, const FiltStat* filt) {
     const int32_t x = draft[b * P.G + t];
     if (!(x >= 0 && x < P.V)) return false;
     const int pidx = b * P.T1 + t;
-    const float px = __expf(logits[(size_t)pidx * P.K * P.V + x] - rowstat[pidx * P.K].logz);
+    const float lx = logits[(size_t)pidx * P.K * P.V + x];
+    float px;
+    if (P.filter) {
+        // the processed target: 0 off the kept set, renormalised on it
+        const FiltStat f = filt[pidx];
+        px = lx >= f.thresh ? __expf(lx - f.logz) : 0.0f;
+    } else {
+        px = __expf(lx - rowstat[pidx * P.K].logz);
+    }
     const float qx = q_hat[(size_t)(b * P.G + t) * P.V + x];
     const u32x4 r = philox10(u32x4{0u, (uint32_t)pidx, 0u, kStreamAccept}, P.key0, P.key1);
     const float u = (float)(r.x >> 8) * 5.9604644775390625e-08f;  // 2^-24
@@ -1156,7 +1166,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const Plan P, const int32_t* __restrict__ draft, const float* __restrict__ q_hat,
     const float* __restrict__ logits, const RowStat* __restrict__ rowstat, const RowStat* __restrict__ centstat,
-    float* __restrict__ jspart, unsigned long long* __restrict__ race_best) {
+    float* __restrict__ jspart, unsigned long long* __restrict__ race_best, const FiltStat* __restrict__ filt) {
     __shared__ float s_red[kVocabWaves][kMaxK + 1];
     __shared__ int s_A;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1176,14 +1186,19 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const int r = blk / P.race_chunks, c = blk - r * P.race_chunks;
     const int b = select_of(P.lossless_bits, P.B, r, true);
     if (wave == 0) {
-        const bool reject = lane < G && !lossless_accept(P, b, lane, draft, q_hat, logits, rowstat);
+        const bool reject = lane < G && !lossless_accept(P, b, lane, draft, q_hat, logits, rowstat, filt);
         const int A = first_reject(reject, G);
         if (lane == 0) s_A = A;
     }
     __syncthreads();
     const int A = s_A;
     const int pidx = b * T1 + A;
-    const float logz = rowstat[pidx * K].logz;
+    float logz = rowstat[pidx * K].logz, thresh = -INFINITY;
+    if (P.filter) {
+        const FiltStat f = filt[pidx];
+        logz = f.logz;
+        thresh = f.thresh;
+    }
     const float* lrow = logits + (size_t)pidx * K * V;
     const float* qrow = A < G ? q_hat + (size_t)(b * G + A) * V : nullptr;
     unsigned long long best_r = 0ull, best_p = 0ull;
@@ -1203,7 +1218,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
         for (int k = 0; k < 4; ++k) {
             const int v = vq + k;
             if (v >= v1) continue;
-            const float p = __expf(lv[k] - logz);
+            const float p = lv[k] >= thresh ? __expf(lv[k] - logz) : 0.0f;
             const float w = qrow ? fmaxf(p - qv[k], 0.0f) : p;
             // U in (0, 1): top 23 bits plus one half, times 2^-23
             const float U = ((float)(words[k] >> 9) + 0.5f) * 1.1920928955078125e-07f;
@@ -1248,6 +1263,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                                                            const RowStat* __restrict__ centstat,
                                                            const float* __restrict__ jspart,
                                                            unsigned long long* __restrict__ race_best,
+                                                           const FiltStat* __restrict__ filt,
                                                            int32_t* __restrict__ accept_len,
                                                            int32_t* __restrict__ out_token,
                                                            uint8_t* __restrict__ dbg_flags,
@@ -1312,7 +1328,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
     bool accept = false;
     if (lane < G) {
         if (lossless) {
-            accept = lossless_accept(P, b, lane, draft, q_hat, logits, rowstat);
+            accept = lossless_accept(P, b, lane, draft, q_hat, logits, rowstat, filt);
         } else {
             int count = 0;
 #pragma unroll
@@ -1344,6 +1360,251 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
         } else {
             out_token[b] = token_lossy;
         }
+    }
+}
+
+// =====================================================================
+// k_filter: the processed target distribution of every lossless position.
+// "Why speculative decoding preserves distributions but may not be faster",
+// Sec. 1: p must already include top-k, top-p and the renormalisation;
+// "Speculative Decoding: Draft, Then Verify", "The same sampling settings":
+// the test and the residual use the processed p.  The pages name the filters
+// without fixing ties; the readings: top-k keeps every token whose logit is
+// >= the k-th largest, top-p keeps the tokens of that set whose strictly
+// larger renormalised mass is below top_p.  Both are thresholds on the
+// logit, found exactly by a radix search over (coarse bin, 32-bit key):
+//   level 0   256 bins by distance below the row max (1/8 logit each, the
+//             lowest bin taking the tail): a monotone function of the logit
+//             that spreads the row over many bins, so that LDS atomics
+//             rarely collide;
+//   levels 1-4  the bytes of the order-preserving key of the logit, most
+//             significant first, among the members of the chosen coarse bin
+//             (gathered into LDS when they fit, else read again from the row).
+// Histograms count tokens and add their masses e^(l - logZ) in 2^-60 fixed
+// point, so every sum is exact and independent of the order of the atomics.
+// One block per position writes the logit threshold, the log normaliser of
+// the kept set and its size.
+// =====================================================================
+constexpr int kFilterThreads = 256;
+constexpr int kFilterWaves = kFilterThreads / 64;
+constexpr int kFilterCache = 4096;  // coarse-bin members held in LDS
+constexpr float kFilterBinsPerUnit = 8.0f;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ int coarse_bin(float l, float m) {
+    return 255 - (int)fminf(fmaxf((m - l) * kFilterBinsPerUnit, 0.0f), 255.0f);
+}
+__device__ __forceinline__ unsigned long long fixed_mass(float l, float logz) {
+    return (unsigned long long)(__expf(l - logz) * 1.152921504606846976e18f);  // 2^60
+}
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long x, int d) {
+    const unsigned lo = __shfl_up((unsigned)x, d, 64), hi = __shfl_up((unsigned)(x >> 32), d, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long shfl_u64(unsigned long long x, int src) {
+    const unsigned lo = __shfl((unsigned)x, src, 64), hi = __shfl((unsigned)(x >> 32), src, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+struct FilterSel {
+    int bin;
+    unsigned cnt_above, cnt_bin;
+    unsigned long long mass_above, mass_bin, total;
+};
+
+struct FilterLds {
+    unsigned cnt[kFilterWaves][256];
+    unsigned long long mass[kFilterWaves][256];
+    uint32_t c_key[kFilterCache];
+    unsigned long long c_mass[kFilterCache];
+    int n_cache;
+    FilterSel sel;
+};
+
+// Wave 0: merges the per-wave histograms and picks the bin.  Count mode: the
+// bin holding rank kk (1-based, from the top) of the range.  Mass mode: the
+// lowest non-empty bin whose tokens above it (base + bins above) weigh less
+// than `target`; `target` < 0 asks for target = top_p * (total of this
+// histogram), the level-0 case.
+__device__ void filter_select(FilterLds& L, bool mass_mode, unsigned kk, unsigned long long base,
+                              unsigned long long target, double top_p, bool level0) {
+    const int lane = threadIdx.x & 63;
+    unsigned c[4];
+    unsigned long long m[4];
+    unsigned tc = 0;
+    unsigned long long tm = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int bin = 255 - 4 * lane - e;  // lane 0 holds the top bins
+        c[e] = 0;
+        m[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kFilterWaves; ++w) {
+            c[e] += L.cnt[w][bin];
+            m[e] += L.mass[w][bin];
+        }
+        tc += c[e];
+        tm += m[e];
+    }
+    unsigned ic = tc;
+    unsigned long long im = tm;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned oc = __shfl_up(ic, d, 64);
+        const unsigned long long om = shfl_up_u64(im, d);
+        if (lane >= d) {
+            ic += oc;
+            im += om;
+        }
+    }
+    const unsigned long long total = shfl_u64(im, 63);
+    if (mass_mode && level0) target = (unsigned long long)(top_p * (double)total);
+    unsigned ac = ic - tc;
+    unsigned long long am = im - tm;
+    int found = -1;
+    unsigned f_ac = 0, f_c = 0;
+    unsigned long long f_am = 0, f_m = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool hit = mass_mode ? (c[e] > 0 && base + am < target) : (ac < kk && kk <= ac + c[e]);
+        if (hit) {  // mass mode keeps the last (lowest) qualifying bin of the lane
+            found = 255 - 4 * lane - e;
+            f_ac = ac;
+            f_am = am;
+            f_c = c[e];
+            f_m = m[e];
+        }
+        ac += c[e];
+        am += m[e];
+    }
+    const unsigned long long any = __ballot(found >= 0);
+    const int src = any ? 63 - __clzll((long long)any) : 0;  // the lowest bins sit in the highest lane
+    if (lane == src) L.sel = FilterSel{found, f_ac, f_c, f_am, f_m, total};
+}
+
+// One radix search over the row's tokens with key >= lo_key.  Returns the
+// final key, and the count and fixed-point mass of the tokens at or above it.
+__device__ void filter_search(FilterLds& L, const float* __restrict__ row, int V, float m, float logz,
+                              uint32_t lo_key, bool mass_mode, unsigned kk, double top_p, uint32_t* key_out,
+                              unsigned* cnt_out, unsigned long long* mass_out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int cb_sel = 0;
+    uint32_t prefix = 0;
+    unsigned base_c = 0;
+    unsigned long long base_m = 0, target = 0;
+    bool cached = false;
+    for (int level = 0; level < 5; ++level) {
+        for (int i = threadIdx.x; i < kFilterWaves * 256; i += kFilterThreads) {
+            (&L.cnt[0][0])[i] = 0u;
+            (&L.mass[0][0])[i] = 0ull;
+        }
+        __syncthreads();
+        const int shift = 24 - 8 * (level - 1);  // key byte of levels 1..4
+        auto add = [&](uint32_t key, float l, unsigned long long ms) {
+            int bin;
+            if (level == 0) {
+                bin = coarse_bin(l, m);
+            } else {
+                if (level > 1 && (key >> (shift + 8)) != prefix) return;
+                bin = (key >> shift) & 255;
+            }
+            atomicAdd(&L.cnt[wave][bin], 1u);
+            atomicAdd(&L.mass[wave][bin], ms);
+        };
+        if (cached) {
+            for (int i = threadIdx.x; i < L.n_cache; i += kFilterThreads) add(L.c_key[i], 0.0f, L.c_mass[i]);
+        } else {
+            for (int v = threadIdx.x; v < V; v += kFilterThreads) {
+                const float l = row[v];
+                const uint32_t key = order_key(l);
+                if (key < lo_key) continue;
+                if (level > 0 && coarse_bin(l, m) != cb_sel) continue;
+                add(key, l, fixed_mass(l, logz));
+            }
+        }
+        __syncthreads();
+        if (wave == 0) filter_select(L, mass_mode, kk, base_m, target, top_p, level == 0);
+        __syncthreads();
+        const FilterSel sel = L.sel;
+        if (level == 0 && mass_mode) target = (unsigned long long)(top_p * (double)sel.total);
+        base_c += sel.cnt_above;
+        base_m += sel.mass_above;
+        if (!mass_mode) kk -= sel.cnt_above;
+        if (level == 0) {
+            cb_sel = sel.bin;
+        } else {
+            prefix = (prefix << 8) | (uint32_t)sel.bin;
+        }
+        if (level == 4) {
+            *key_out = prefix;
+            *cnt_out = base_c + sel.cnt_bin;
+            *mass_out = base_m + sel.mass_bin;
+        }
+        if (level == 0 && sel.cnt_bin <= (unsigned)kFilterCache) {
+            // gather the chosen coarse bin's members (one slot claim per wave step)
+            if (threadIdx.x == 0) L.n_cache = 0;
+            __syncthreads();
+            for (int v0 = 0; v0 < V; v0 += kFilterThreads) {
+                const int v = v0 + threadIdx.x;
+                bool mem = false;
+                float l = 0.0f;
+                uint32_t key = 0;
+                if (v < V) {
+                    l = row[v];
+                    key = order_key(l);
+                    mem = key >= lo_key && coarse_bin(l, m) == cb_sel;
+                }
+                const unsigned long long bal = __ballot(mem);
+                if (bal) {
+                    int slot0 = 0;
+                    if (lane == 0) slot0 = atomicAdd(&L.n_cache, __popcll(bal));
+                    slot0 = __shfl(slot0, 0, 64);
+                    if (mem) {
+                        const int slot = slot0 + __popcll(bal & ((1ull << lane) - 1ull));
+                        L.c_key[slot] = key;
+                        L.c_mass[slot] = fixed_mass(l, logz);
+                    }
+                }
+            }
+            __syncthreads();
+            cached = true;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kFilterThreads) void k_filter(const Plan P, const float* __restrict__ logits,
+                                                           const RowStat* __restrict__ rowstat,
+                                                           FiltStat* __restrict__ filt,
+                                                           int32_t* __restrict__ dbg_count,
+                                                           float* __restrict__ dbg_logz) {
+    __shared__ FilterLds L;
+    const int r = blockIdx.x / P.T1, t = blockIdx.x - r * P.T1;
+    const int b = select_of(P.lossless_bits, P.B, r, true);
+    const int pidx = b * P.T1 + t;
+    const float* row = logits + (size_t)pidx * P.K * P.V;
+    const RowStat rs = rowstat[pidx * P.K];
+    const bool use_k = P.top_k > 0 && P.top_k < P.V;
+    const bool use_p = P.top_p > 0.0f && P.top_p < 1.0f;
+
+    uint32_t key = 0u, lo_key = 0u;
+    unsigned cnt = (unsigned)P.V;
+    unsigned long long mass = 0ull;
+    if (use_k) {
+        filter_search(L, row, P.V, rs.m, rs.logz, 0u, false, (unsigned)P.top_k, 0.0, &key, &cnt, &mass);
+        lo_key = key;
+    }
+    if (use_p) filter_search(L, row, P.V, rs.m, rs.logz, lo_key, true, 0u, (double)P.top_p, &key, &cnt, &mass);
+    if (threadIdx.x == 0) {
+        const float lz = (float)((double)rs.logz + log((double)mass * 8.673617379884035e-19));  // 2^-60
+        filt[pidx] = FiltStat{key_value(key), lz, (int)cnt, 0};
+        if (dbg_count) dbg_count[pidx] = (int)cnt;
+        if (dbg_logz) dbg_logz[pidx] = lz;
     }
 }
 
@@ -1454,19 +1715,26 @@ hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, Row
     return hipGetLastError();
 }
 
+hipError_t launch_filter(const Plan& P, const float* logits, const RowStat* rowstat, FiltStat* filt,
+                         int32_t* dbg_count, float* dbg_logz, hipStream_t st) {
+    if (!P.filter || P.n_lossless_seq == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_filter, dim3(P.n_lossless_seq * P.T1), dim3(kFilterThreads), 0, st, P, logits, rowstat, filt,
+                       dbg_count, dbg_logz);
+    return hipGetLastError();
+}
+
 hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const float* logits,
                         const RowStat* rowstat, const RowStat* centstat, float* jspart,
-                        unsigned long long* race_best, int32_t* accept_len, int32_t* out_token, uint8_t* dbg_flags,
-                        float* dbg_js_heads, float* dbg_js_draft, hipStream_t st) {
+                        unsigned long long* race_best, const FiltStat* filt, int32_t* accept_len, int32_t* out_token,
+                        uint8_t* dbg_flags, float* dbg_js_heads, float* dbg_js_draft, hipStream_t st) {
     if (P.blk_js + P.blk_race > 0) {
         hipLaunchKernelGGL(k_vocab, dim3(P.blk_js + P.blk_race), dim3(kVocabThreads), 0, st, P, draft, q_hat, logits,
-                           rowstat, centstat, jspart, race_best);
+                           rowstat, centstat, jspart, race_best, filt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishThreads), 0, st, P, draft, q_hat, logits, rowstat, centstat,
-                       jspart,
-                       race_best, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
+                       jspart, race_best, filt, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
 }
 

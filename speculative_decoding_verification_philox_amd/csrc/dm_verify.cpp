@@ -27,6 +27,7 @@ struct dm_verify {
     RowMeta* meta;
     float* jspart;
     unsigned long long* race;
+    FiltStat* filt;
     size_t cap_hm, cap_part, cap_jspart, cap_meta_rows;
     hipEvent_t prof_start, prof_stop;
 };
@@ -60,6 +61,9 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
     if (a->batch < 1 || a->batch > D->max_batch) return DM_ERR_INVALID_ARGUMENT;
     if (a->K < 1 || a->K > D->k_max) return DM_ERR_INVALID_ARGUMENT;
     if (!(a->p_drop >= 0.0f && a->p_drop < 1.0f)) return DM_ERR_INVALID_ARGUMENT;
+    if (!(a->temperature >= 0.0f) || !std::isfinite(a->temperature)) return DM_ERR_INVALID_ARGUMENT;
+    if (a->top_k < 0 || !(a->top_p >= 0.0f) || !std::isfinite(a->top_p) || a->reserved != 0)
+        return DM_ERR_INVALID_ARGUMENT;
     if (!a->W || !a->h || !a->modes || !a->accept_len || !a->out_token) return DM_ERR_INVALID_ARGUMENT;
     if (D->gamma > 0 && !a->draft) return DM_ERR_INVALID_ARGUMENT;
     bool need_q = false;
@@ -71,7 +75,8 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
     if (need_q && D->gamma > 0 && !a->q_hat) return DM_ERR_INVALID_ARGUMENT;
     if (!aligned(a->W, 16) || !aligned(a->h, 16)) return DM_ERR_UNSUPPORTED;
     const void* four[] = {a->draft, a->q_hat, a->accept_len, a->out_token, a->head_argmax, a->centroid_argmax,
-                          a->head_logz, a->centroid_logz, a->js_heads, a->js_draft, a->logits, a->mask_bits};
+                          a->head_logz, a->centroid_logz, a->js_heads, a->js_draft, a->logits, a->mask_bits,
+                          a->filter_count, a->filter_logz};
     for (const void* p : four)
         if (p && !aligned(p, 4)) return DM_ERR_UNSUPPORTED;
     return DM_OK;
@@ -186,7 +191,7 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
 }
 
 struct Sizes {
-    size_t hm, logits, part, rowstat, centstat, meta, jspart, race;
+    size_t hm, logits, part, rowstat, centstat, meta, jspart, race, filt;
 };
 
 Sizes workspace_sizes(const dm_verify_desc& D) {
@@ -218,13 +223,15 @@ Sizes workspace_sizes(const dm_verify_desc& D) {
     s.meta = max_hm_rows * sizeof(RowMeta);
     s.jspart = (max_js > 0 ? max_js : 1) * sizeof(float);
     s.race = (size_t)D.max_batch * 2 * sizeof(unsigned long long);
+    s.filt = (size_t)D.max_batch * T1 * sizeof(FiltStat);
     return s;
 }
 
 size_t total_bytes(const Sizes& s) {
     const size_t a = 256;
     return align_up(s.hm, a) + align_up(s.logits, a) + align_up(s.part, a) + align_up(s.rowstat, a) +
-           align_up(s.centstat, a) + align_up(s.meta, a) + align_up(s.jspart, a) + align_up(s.race, a);
+           align_up(s.centstat, a) + align_up(s.meta, a) + align_up(s.jspart, a) + align_up(s.race, a) +
+           align_up(s.filt, a);
 }
 
 }  // namespace
@@ -287,6 +294,7 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
     h->meta = (RowMeta*)take(s.meta);
     h->jspart = (float*)take(s.jspart);
     h->race = (unsigned long long*)take(s.race);
+    h->filt = (FiltStat*)take(s.filt);
     // The race winners start at zero; the kernel that consumes them clears
     // them at the end of every call.
     e = hipMemset(h->race, 0, s.race);
@@ -354,7 +362,13 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
         if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
     }
-    P.scale = (float)(1.0 / (1.0 - (double)a->p_drop));
+    // temperature divides every row: folded into the row scales
+    const double temp = a->temperature > 0.0f ? (double)a->temperature : 1.0;
+    P.scale = (float)(1.0 / ((1.0 - (double)a->p_drop) * temp));
+    P.scale_undropped = (float)(1.0 / temp);
+    P.top_k = a->top_k;
+    P.top_p = a->top_p;
+    P.filter = n_lossless > 0 && ((a->top_k > 0 && a->top_k < D.vocab) || (a->top_p > 0.0f && a->top_p < 1.0f));
     P.inv_k = 1.0f / (float)a->K;
     P.thresh = drop_threshold(a->p_drop);
     P.key0 = (uint32_t)(a->seed & 0xffffffffu);
@@ -391,8 +405,9 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     }
     DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, a->head_argmax, a->head_logz, a->centroid_argmax,
                           a->centroid_logz, st));
-    DM_TRY(launch_vocab(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, h->race, a->accept_len,
-                        a->out_token, a->accept_flags, a->js_heads, a->js_draft, st));
+    DM_TRY(launch_filter(P, logits, h->rowstat, h->filt, a->filter_count, a->filter_logz, st));
+    DM_TRY(launch_vocab(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, h->race, h->filt,
+                        a->accept_len, a->out_token, a->accept_flags, a->js_heads, a->js_draft, st));
 #undef DM_TRY
     return DM_OK;
 }

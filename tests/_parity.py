@@ -5,7 +5,12 @@ Parity bar (from the verify step's contract):
   * dropout masks, argmaxes and emitted tokens bit-exact;
   * logits within 2e-2 absolute, JS values within 1e-5 absolute;
   * accept decisions identical except where the oracle's margin is below
-    1e-4 (such near-ties are counted and reported).
+    1e-4 (such near-ties are counted and reported);
+  * with top-k / top-p on, the kept-set size of every lossless position
+    identical and its log normaliser within 1e-3, except where the oracle's
+    filter margin (logit gap at the k-th value, mass gap at the top-p
+    boundary) is below 2e-3; such positions also exempt their decision and,
+    at A, the emitted token.
 An argmax (or emitted token) may differ only where the oracle's top-2 gap is
 below the same 1e-4 (the fp32 path cannot order closer values reliably);
 those are counted too.
@@ -25,6 +30,7 @@ JS_TOL = 1e-5
 LOGZ_TOL = 1e-3
 MARGIN = 1e-4
 RACE_GAP = 1e-3
+FILTER_MARGIN = 2e-3
 
 
 def gpu_available():
@@ -90,11 +96,11 @@ def weights(ver, inp: Inputs, layout):
     return inp.W
 
 
-def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR):
+def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None):
     import torch
 
     out = ver.run(weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug,
-                  w_layout=layout)
+                  w_layout=layout, **(sampling or {}))
     torch.cuda.synchronize()
     res = {}
     for k, v in out.items():
@@ -117,6 +123,8 @@ class Report:
     max_logit_err: float = 0.0
     max_js_err: float = 0.0
     max_logz_err: float = 0.0
+    filter_positions: int = 0
+    filter_near_ties: int = 0
 
     def add(self, o: "Report"):
         for f in dataclasses.fields(self):
@@ -124,9 +132,10 @@ class Report:
             setattr(self, f.name, max(a, b) if f.name.startswith("max_") else a + b)
 
 
-def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
+def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False) -> Report:
     """Assert the parity bar; returns the near-tie accounting.  `seqs` are the
-    batch indices the oracle evaluated (its rows, in order)."""
+    batch indices the oracle evaluated (its rows, in order).  `filtered`: a
+    top-k / top-p filter was on."""
     modes = np.asarray(modes)
     n = ora["accept_len"].shape[0]
     seqs = np.arange(n) if seqs is None else np.asarray(seqs)
@@ -135,6 +144,21 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
     for r, b in enumerate(seqs):
         mode = int(modes[b])
         rows = K if mode != wl.LOSSLESS else 1
+        fnear = np.zeros(G + 1, bool)
+        if filtered and mode == wl.LOSSLESS:
+            fnear = ora["filter_margin"][r] < FILTER_MARGIN
+            rep.filter_positions += G + 1
+            rep.filter_near_ties += int(fnear.sum())
+            if "filter_count" in gpu:
+                gcnt, ocnt = gpu["filter_count"][b], ora["filter_count"][r]
+                bad = gcnt != ocnt
+                assert np.all(fnear[bad]), (
+                    f"kept-set size of sequence {b}: gpu {gcnt[bad & ~fnear]} oracle {ocnt[bad & ~fnear]}")
+                same = ~bad
+                lz = np.abs(gpu["filter_logz"][b][same] - ora["filter_logz"][r][same])
+                lz = float(lz.max()) if lz.size else 0.0
+                rep.max_logz_err = max(rep.max_logz_err, lz)
+                assert lz <= LOGZ_TOL, f"kept-set log normaliser of sequence {b} off by {lz}"
         if check_debug:
             if "mask_bits" in gpu and "mask_bits" in ora:
                 np.testing.assert_array_equal(gpu["mask_bits"][b, :, :rows], ora["mask_bits"][r, :, :rows],
@@ -165,7 +189,7 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
                 assert max(e1, e2) <= JS_TOL, f"JS of sequence {b} off by {max(e1, e2)}"
         # decisions
         margin = ora["margin"][r]
-        near = margin < MARGIN
+        near = (margin < MARGIN) | fnear[:G]
         rep.decisions += G
         rep.decision_near_ties += int(near.sum())
         if "accept_flags" in gpu:
@@ -179,7 +203,7 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
         rep.sequences += 1
         decisive = near[: min(A_o + 1, G)].any() if G > 0 else False
         if mode == wl.LOSSLESS:
-            tok_near = ora["race_gap"][r] < RACE_GAP
+            tok_near = ora["race_gap"][r] < RACE_GAP or bool(fnear[A_o])
         else:
             tok_near = ora["centroid_gap"][r][A_o] < MARGIN
         if decisive or tok_near:
@@ -191,6 +215,6 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True) -> Report:
     return rep
 
 
-def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True):
+def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None):
     return oracle.run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=seqs, want_logits=debug,
-                      want_masks=debug and W.shape[1] % 32 == 0)
+                      want_masks=debug and W.shape[1] % 32 == 0, **(sampling or {}))

@@ -16,8 +16,12 @@ hipError_t launch_gemm(const Plan&, const void*, const void*, const RowMeta*, fl
 }
 hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*, float*, int32_t*, float*,
                           hipStream_t) { return hipSuccess; }
+hipError_t launch_filter(const Plan&, const float*, const RowStat*, FiltStat*, int32_t*, float*, hipStream_t) {
+    return hipSuccess;
+}
 hipError_t launch_vocab(const Plan&, const int32_t*, const float*, const float*, const RowStat*, const RowStat*,
-                        float*, unsigned long long*, int32_t*, int32_t*, uint8_t*, float*, float*, hipStream_t) {
+                        float*, unsigned long long*, const FiltStat*, int32_t*, int32_t*, uint8_t*, float*, float*,
+                        hipStream_t) {
     return hipSuccess;
 }
 hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipSuccess; }

@@ -48,8 +48,9 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header(lib):
     # sizes follow from the field lists in include/dm_verify.h on LP64
     assert ctypes.sizeof(B.dm_verify_desc) == 24
-    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 2 * 8 + 9 * 8
+    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 2 * 8 + 11 * 8
     assert B.dm_verify_args.seed.offset == 56
+    assert B.dm_verify_args.temperature.offset == 64 and B.dm_verify_args.accept_len.offset == 80
 
 
 def desc(**kw):
@@ -118,9 +119,24 @@ def test_bad_desc(lib, field, value, status):
     (dict(W=0x10008), B.DM_ERR_UNSUPPORTED),
     (dict(h=0x10004), B.DM_ERR_UNSUPPORTED),
     (dict(q_hat=0x10002), B.DM_ERR_UNSUPPORTED),
+    (dict(temperature=-0.5), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(temperature=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(temperature=float("inf")), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(top_k=-1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(top_p=-0.1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(top_p=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(filter_count=0x10002), B.DM_ERR_UNSUPPORTED),
 ])
 def test_bad_args(lib, change, status):
     assert B.dm_verify_check(desc(), args(**change)) == status
+
+
+@pytest.mark.parametrize("change", [dict(temperature=0.0), dict(temperature=0.7), dict(temperature=3.0),
+                                    dict(top_k=1), dict(top_k=100000), dict(top_p=0.9), dict(top_p=1.0),
+                                    dict(top_p=2.0), dict(top_k=5, top_p=0.5, temperature=0.8)])
+def test_sampling_settings_in_range_pass(lib, change):
+    assert B.dm_verify_check(desc(), args(**change)) == B.DM_OK
 
 
 def test_mode_out_of_range(lib):
