@@ -1372,23 +1372,25 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
 // without fixing ties; the readings: top-k keeps every token whose logit is
 // >= the k-th largest, top-p keeps the tokens of that set whose strictly
 // larger renormalised mass is below top_p.  Both are thresholds on the
-// logit, found exactly by a radix search over (coarse bin, 32-bit key):
-//   level 0   256 bins by distance below the row max (1/8 logit each, the
-//             lowest bin taking the tail): a monotone function of the logit
-//             that spreads the row over many bins, so that LDS atomics
-//             rarely collide;
-//   levels 1-4  the bytes of the order-preserving key of the logit, most
-//             significant first, among the members of the chosen coarse bin
-//             (gathered into LDS when they fit, else read again from the row).
+// logit, found exactly by a radix search over the lexicographic order
+// (distance bin, 32-bit key), which is the order of the logits:
+//   F = floor((max - l) * 2048), clamped to 16 bits, is a monotone function
+//   of the logit; level 0 bins its high byte (1/8 logit per bin), level 1
+//   its low byte, levels 2-5 the bytes of the order-preserving key.
+// The distance bins spread a row over many bins (few LDS atomic collisions)
+// and shrink the candidate range fast: once the range holds at most
+// kFilterCache tokens they are gathered into LDS and the remaining levels
+// read only that copy.  When the top-k set itself fits, it is gathered
+// whole and the top-p search never reads the row again.
 // Histograms count tokens and add their masses e^(l - logZ) in 2^-60 fixed
 // point, so every sum is exact and independent of the order of the atomics.
 // One block per position writes the logit threshold, the log normaliser of
 // the kept set and its size.
 // =====================================================================
-constexpr int kFilterThreads = 256;
-constexpr int kFilterWaves = kFilterThreads / 64;
-constexpr int kFilterCache = 4096;  // coarse-bin members held in LDS
-constexpr float kFilterBinsPerUnit = 8.0f;
+constexpr int kFilterThreads = 1024;
+constexpr int kFilterHists = 4;     // histogram copies (wave % 4) to spread the atomics
+constexpr int kFilterCache = 8192;  // candidate tokens held in LDS
+constexpr int kFilterUnroll = 8;    // row loads in flight per thread
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
@@ -1397,8 +1399,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
-__device__ __forceinline__ int coarse_bin(float l, float m) {
-    return 255 - (int)fminf(fmaxf((m - l) * kFilterBinsPerUnit, 0.0f), 255.0f);
+__device__ __forceinline__ int dist_index(float l, float m) {
+    return (int)fminf(fmaxf((m - l) * 2048.0f, 0.0f), 65535.0f);
 }
 __device__ __forceinline__ unsigned long long fixed_mass(float l, float logz) {
     return (unsigned long long)(__expf(l - logz) * 1.152921504606846976e18f);  // 2^60
@@ -1419,21 +1421,40 @@ struct FilterSel {
 };
 
 struct FilterLds {
-    unsigned cnt[kFilterWaves][256];
-    unsigned long long mass[kFilterWaves][256];
+    unsigned cnt[kFilterHists][256];
+    unsigned long long mass[kFilterHists][256];
     uint32_t c_key[kFilterCache];
     unsigned long long c_mass[kFilterCache];
     int n_cache;
     FilterSel sel;
 };
 
-// Wave 0: merges the per-wave histograms and picks the bin.  Count mode: the
+// The candidate range of a search: tokens with key >= lo and, from level 1
+// on, distance bytes and key bytes equal to the ones chosen so far.
+struct FilterRange {
+    uint32_t lo;
+    int level, hi_byte, lo_byte;
+    uint32_t prefix;
+    __device__ bool contains(int F, uint32_t key) const {
+        if (key < lo) return false;
+        if (level >= 1 && (F >> 8) != hi_byte) return false;
+        if (level >= 2 && (F & 255) != lo_byte) return false;
+        if (level >= 3 && (key >> (32 - 8 * (level - 2))) != prefix) return false;
+        return true;
+    }
+    __device__ int bin(int F, uint32_t key) const {
+        if (level == 0) return 255 - (F >> 8);
+        if (level == 1) return 255 - (F & 255);
+        return (int)((key >> (24 - 8 * (level - 2))) & 255u);
+    }
+};
+
+// Wave 0: merges the histogram copies and picks the bin.  Count mode: the
 // bin holding rank kk (1-based, from the top) of the range.  Mass mode: the
 // lowest non-empty bin whose tokens above it (base + bins above) weigh less
-// than `target`; `target` < 0 asks for target = top_p * (total of this
-// histogram), the level-0 case.
+// than the target; at the first level the target is top_p times the total.
 __device__ void filter_select(FilterLds& L, bool mass_mode, unsigned kk, unsigned long long base,
-                              unsigned long long target, double top_p, bool level0) {
+                              unsigned long long target, double top_p, bool first) {
     const int lane = threadIdx.x & 63;
     unsigned c[4];
     unsigned long long m[4];
@@ -1445,7 +1466,7 @@ __device__ void filter_select(FilterLds& L, bool mass_mode, unsigned kk, unsigne
         c[e] = 0;
         m[e] = 0;
 #pragma unroll
-        for (int w = 0; w < kFilterWaves; ++w) {
+        for (int w = 0; w < kFilterHists; ++w) {
             c[e] += L.cnt[w][bin];
             m[e] += L.mass[w][bin];
         }
@@ -1464,7 +1485,7 @@ __device__ void filter_select(FilterLds& L, bool mass_mode, unsigned kk, unsigne
         }
     }
     const unsigned long long total = shfl_u64(im, 63);
-    if (mass_mode && level0) target = (unsigned long long)(top_p * (double)total);
+    if (mass_mode && first) target = (unsigned long long)(top_p * (double)total);
     unsigned ac = ic - tc;
     unsigned long long am = im - tm;
     int found = -1;
@@ -1488,91 +1509,136 @@ __device__ void filter_select(FilterLds& L, bool mass_mode, unsigned kk, unsigne
     if (lane == src) L.sel = FilterSel{found, f_ac, f_c, f_am, f_m, total};
 }
 
-// One radix search over the row's tokens with key >= lo_key.  Returns the
-// final key, and the count and fixed-point mass of the tokens at or above it.
-__device__ void filter_search(FilterLds& L, const float* __restrict__ row, int V, float m, float logz,
-                              uint32_t lo_key, bool mass_mode, unsigned kk, double top_p, uint32_t* key_out,
+// Calls f(F, key, mass) for every token of the row in `range`, reading the
+// row with kFilterUnroll loads in flight per thread (16-byte loads when the
+// rows are 16-byte aligned: the pass is bound by the bytes in flight).
+template <typename Fn>
+__device__ __forceinline__ void for_row(const float* __restrict__ row, int V, bool vec4, float m, float logz,
+                                        const FilterRange& range, Fn f) {
+    if (vec4) {
+        const v4f* row4 = reinterpret_cast<const v4f*>(row);
+        const int V4 = V >> 2;
+        for (int u0 = 0; u0 < V4; u0 += kFilterThreads * kFilterUnroll) {
+            v4f x[kFilterUnroll];
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) {
+                const int u = u0 + j * kFilterThreads + threadIdx.x;
+                x[j] = u < V4 ? row4[u] : v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) {
+                const int u = u0 + j * kFilterThreads + threadIdx.x;
+                if (u >= V4) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = order_key(x[j][e]);
+                    const int F = dist_index(x[j][e], m);
+                    if (range.contains(F, key)) f(F, key, fixed_mass(x[j][e], logz));
+                }
+            }
+        }
+        return;
+    }
+    for (int v0 = 0; v0 < V; v0 += kFilterThreads * kFilterUnroll) {
+        float l[kFilterUnroll];
+#pragma unroll
+        for (int j = 0; j < kFilterUnroll; ++j) {
+            const int v = v0 + j * kFilterThreads + threadIdx.x;
+            l[j] = v < V ? row[v] : -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < kFilterUnroll; ++j) {
+            const int v = v0 + j * kFilterThreads + threadIdx.x;
+            if (v >= V) continue;
+            const uint32_t key = order_key(l[j]);
+            const int F = dist_index(l[j], m);
+            if (range.contains(F, key)) f(F, key, fixed_mass(l[j], logz));
+        }
+    }
+}
+
+// Copies the row's tokens in `range` (at most kFilterCache) into the cache.
+__device__ void filter_gather(FilterLds& L, const float* __restrict__ row, int V, float m, float logz,
+                              const FilterRange& range) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) L.n_cache = 0;
+    __syncthreads();
+    for (int v0 = 0; v0 < V; v0 += kFilterThreads) {
+        const int v = v0 + threadIdx.x;
+        float l = 0.0f;
+        uint32_t key = 0;
+        bool mem = false;
+        if (v < V) {
+            l = row[v];
+            key = order_key(l);
+            mem = range.contains(dist_index(l, m), key);
+        }
+        const unsigned long long bal = __ballot(mem);
+        if (bal) {  // one slot claim per wave step
+            int slot0 = 0;
+            if (lane == 0) slot0 = atomicAdd(&L.n_cache, __popcll(bal));
+            slot0 = __shfl(slot0, 0, 64);
+            if (mem) {
+                const int slot = slot0 + __popcll(bal & ((1ull << lane) - 1ull));
+                L.c_key[slot] = key;
+                L.c_mass[slot] = fixed_mass(l, logz);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// One radix search over the tokens with key >= lo.  `cached`: the cache
+// already holds exactly those tokens.  Returns the final key and the count
+// and fixed-point mass of the tokens at or above it.
+__device__ void filter_search(FilterLds& L, const float* __restrict__ row, int V, bool vec4, float m, float logz,
+                              uint32_t lo, bool cached, bool mass_mode, unsigned kk, double top_p, uint32_t* key_out,
                               unsigned* cnt_out, unsigned long long* mass_out) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int cb_sel = 0;
-    uint32_t prefix = 0;
+    const int hist = (threadIdx.x >> 6) & (kFilterHists - 1);
+    FilterRange range{lo, 0, 0, 0, 0u};
     unsigned base_c = 0;
     unsigned long long base_m = 0, target = 0;
-    bool cached = false;
-    for (int level = 0; level < 5; ++level) {
-        for (int i = threadIdx.x; i < kFilterWaves * 256; i += kFilterThreads) {
+    for (int level = 0; level < 6; ++level) {
+        range.level = level;
+        for (int i = threadIdx.x; i < kFilterHists * 256; i += kFilterThreads) {
             (&L.cnt[0][0])[i] = 0u;
             (&L.mass[0][0])[i] = 0ull;
         }
         __syncthreads();
-        const int shift = 24 - 8 * (level - 1);  // key byte of levels 1..4
-        auto add = [&](uint32_t key, float l, unsigned long long ms) {
-            int bin;
-            if (level == 0) {
-                bin = coarse_bin(l, m);
-            } else {
-                if (level > 1 && (key >> (shift + 8)) != prefix) return;
-                bin = (key >> shift) & 255;
-            }
-            atomicAdd(&L.cnt[wave][bin], 1u);
-            atomicAdd(&L.mass[wave][bin], ms);
+        auto add = [&](int F, uint32_t key, unsigned long long ms) {
+            const int bin = range.bin(F, key);
+            atomicAdd(&L.cnt[hist][bin], 1u);
+            atomicAdd(&L.mass[hist][bin], ms);
         };
         if (cached) {
-            for (int i = threadIdx.x; i < L.n_cache; i += kFilterThreads) add(L.c_key[i], 0.0f, L.c_mass[i]);
-        } else {
-            for (int v = threadIdx.x; v < V; v += kFilterThreads) {
-                const float l = row[v];
-                const uint32_t key = order_key(l);
-                if (key < lo_key) continue;
-                if (level > 0 && coarse_bin(l, m) != cb_sel) continue;
-                add(key, l, fixed_mass(l, logz));
+            for (int i = threadIdx.x; i < L.n_cache; i += kFilterThreads) {
+                const uint32_t key = L.c_key[i];
+                const int F = dist_index(key_value(key), m);
+                if (range.contains(F, key)) add(F, key, L.c_mass[i]);
             }
+        } else {
+            for_row(row, V, vec4, m, logz, range, add);
         }
         __syncthreads();
-        if (wave == 0) filter_select(L, mass_mode, kk, base_m, target, top_p, level == 0);
+        if (threadIdx.x < 64) filter_select(L, mass_mode, kk, base_m, target, top_p, level == 0);
         __syncthreads();
         const FilterSel sel = L.sel;
         if (level == 0 && mass_mode) target = (unsigned long long)(top_p * (double)sel.total);
         base_c += sel.cnt_above;
         base_m += sel.mass_above;
         if (!mass_mode) kk -= sel.cnt_above;
-        if (level == 0) {
-            cb_sel = sel.bin;
-        } else {
-            prefix = (prefix << 8) | (uint32_t)sel.bin;
-        }
-        if (level == 4) {
-            *key_out = prefix;
+        if (level == 0) range.hi_byte = 255 - sel.bin;
+        else if (level == 1) range.lo_byte = 255 - sel.bin;
+        else range.prefix = (range.prefix << 8) | (uint32_t)sel.bin;
+        if (level == 5) {
+            *key_out = range.prefix;
             *cnt_out = base_c + sel.cnt_bin;
             *mass_out = base_m + sel.mass_bin;
-        }
-        if (level == 0 && sel.cnt_bin <= (unsigned)kFilterCache) {
-            // gather the chosen coarse bin's members (one slot claim per wave step)
-            if (threadIdx.x == 0) L.n_cache = 0;
-            __syncthreads();
-            for (int v0 = 0; v0 < V; v0 += kFilterThreads) {
-                const int v = v0 + threadIdx.x;
-                bool mem = false;
-                float l = 0.0f;
-                uint32_t key = 0;
-                if (v < V) {
-                    l = row[v];
-                    key = order_key(l);
-                    mem = key >= lo_key && coarse_bin(l, m) == cb_sel;
-                }
-                const unsigned long long bal = __ballot(mem);
-                if (bal) {
-                    int slot0 = 0;
-                    if (lane == 0) slot0 = atomicAdd(&L.n_cache, __popcll(bal));
-                    slot0 = __shfl(slot0, 0, 64);
-                    if (mem) {
-                        const int slot = slot0 + __popcll(bal & ((1ull << lane) - 1ull));
-                        L.c_key[slot] = key;
-                        L.c_mass[slot] = fixed_mass(l, logz);
-                    }
-                }
-            }
-            __syncthreads();
+        } else if (!cached && sel.cnt_bin <= (unsigned)kFilterCache) {
+            // the next range is the chosen bin: small enough to keep in LDS
+            FilterRange next = range;
+            next.level = level + 1;
+            filter_gather(L, row, V, m, logz, next);
             cached = true;
         }
     }
@@ -1591,15 +1657,24 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(const Plan P, const f
     const RowStat rs = rowstat[pidx * P.K];
     const bool use_k = P.top_k > 0 && P.top_k < P.V;
     const bool use_p = P.top_p > 0.0f && P.top_p < 1.0f;
+    const bool vec4 = P.vec4 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
 
-    uint32_t key = 0u, lo_key = 0u;
+    uint32_t key = 0u, lo = 0u;
     unsigned cnt = (unsigned)P.V;
     unsigned long long mass = 0ull;
+    bool cached = false;
     if (use_k) {
-        filter_search(L, row, P.V, rs.m, rs.logz, 0u, false, (unsigned)P.top_k, 0.0, &key, &cnt, &mass);
-        lo_key = key;
+        filter_search(L, row, P.V, vec4, rs.m, rs.logz, 0u, false, false, (unsigned)P.top_k, 0.0, &key, &cnt,
+                      &mass);
+        lo = key;
+        if (use_p && cnt <= (unsigned)kFilterCache) {
+            // the whole top-k set fits: the top-p search reads only its copy
+            filter_gather(L, row, P.V, rs.m, rs.logz, FilterRange{lo, 0, 0, 0, 0u});
+            cached = true;
+        }
     }
-    if (use_p) filter_search(L, row, P.V, rs.m, rs.logz, lo_key, true, 0u, (double)P.top_p, &key, &cnt, &mass);
+    if (use_p)
+        filter_search(L, row, P.V, vec4, rs.m, rs.logz, lo, cached, true, 0u, (double)P.top_p, &key, &cnt, &mass);
     if (threadIdx.x == 0) {
         const float lz = (float)((double)rs.logz + log((double)mass * 8.673617379884035e-19));  // 2^-60
         filt[pidx] = FiltStat{key_value(key), lz, (int)cnt, 0};
