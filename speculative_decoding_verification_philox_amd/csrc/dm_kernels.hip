@@ -1557,24 +1557,19 @@ __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, bo
     }
 }
 
-// Copies the row's tokens in `range` (at most kFilterCache) into the cache.
-__device__ void filter_gather(FilterLds& L, const float* __restrict__ row, int V, float m, float logz,
+// Copies the row's tokens in `range` (at most kFilterCache) into the cache,
+// with the same loads in flight as for_row; slots are claimed once per wave
+// and value.
+__device__ void filter_gather(FilterLds& L, const float* __restrict__ row, int V, bool vec4, float m, float logz,
                               const FilterRange& range) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x == 0) L.n_cache = 0;
     __syncthreads();
-    for (int v0 = 0; v0 < V; v0 += kFilterThreads) {
-        const int v = v0 + threadIdx.x;
-        float l = 0.0f;
-        uint32_t key = 0;
-        bool mem = false;
-        if (v < V) {
-            l = row[v];
-            key = order_key(l);
-            mem = range.contains(dist_index(l, m), key);
-        }
+    auto put = [&](bool valid, float l) {
+        const uint32_t key = order_key(l);
+        const bool mem = valid && range.contains(dist_index(l, m), key);
         const unsigned long long bal = __ballot(mem);
-        if (bal) {  // one slot claim per wave step
+        if (bal) {
             int slot0 = 0;
             if (lane == 0) slot0 = atomicAdd(&L.n_cache, __popcll(bal));
             slot0 = __shfl(slot0, 0, 64);
@@ -1583,6 +1578,35 @@ __device__ void filter_gather(FilterLds& L, const float* __restrict__ row, int V
                 L.c_key[slot] = key;
                 L.c_mass[slot] = fixed_mass(l, logz);
             }
+        }
+    };
+    if (vec4) {
+        const v4f* row4 = reinterpret_cast<const v4f*>(row);
+        const int V4 = V >> 2;
+        for (int u0 = 0; u0 < V4; u0 += kFilterThreads * kFilterUnroll) {
+            v4f x[kFilterUnroll];
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) {
+                const int u = u0 + j * kFilterThreads + threadIdx.x;
+                x[j] = u < V4 ? row4[u] : v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) {
+                const bool valid = u0 + j * kFilterThreads + (int)threadIdx.x < V4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) put(valid, x[j][e]);
+            }
+        }
+    } else {
+        for (int v0 = 0; v0 < V; v0 += kFilterThreads * kFilterUnroll) {
+            float x[kFilterUnroll];
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) {
+                const int v = v0 + j * kFilterThreads + threadIdx.x;
+                x[j] = v < V ? row[v] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kFilterUnroll; ++j) put(v0 + j * kFilterThreads + (int)threadIdx.x < V, x[j]);
         }
     }
     __syncthreads();
@@ -1638,7 +1662,7 @@ __device__ void filter_search(FilterLds& L, const float* __restrict__ row, int V
             // the next range is the chosen bin: small enough to keep in LDS
             FilterRange next = range;
             next.level = level + 1;
-            filter_gather(L, row, V, m, logz, next);
+            filter_gather(L, row, V, vec4, m, logz, next);
             cached = true;
         }
     }
@@ -1669,7 +1693,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(const Plan P, const f
         lo = key;
         if (use_p && cnt <= (unsigned)kFilterCache) {
             // the whole top-k set fits: the top-p search reads only its copy
-            filter_gather(L, row, P.V, rs.m, rs.logz, FilterRange{lo, 0, 0, 0, 0u});
+            filter_gather(L, row, P.V, vec4, rs.m, rs.logz, FilterRange{lo, 0, 0, 0, 0u});
             cached = true;
         }
     }
