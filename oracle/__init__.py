@@ -38,6 +38,7 @@ class _Problem(ctypes.Structure):
         ("q_hat", _c_f32p), ("modes", _c_u8p), ("n_seq", ctypes.c_int32),
         ("n_threads", ctypes.c_int32), ("seq", _c_i32p), ("temperature", ctypes.c_float),
         ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("pad1", ctypes.c_uint32),
+        ("seq_gamma", _c_i32p), ("seq_K", _c_i32p), ("seq_p_drop", _c_f32p),
     ]
 
 
@@ -178,14 +179,16 @@ def processed(l, top_k=0, top_p=0.0):
 
 # -------------------------------------------------------------- full verify
 def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False,
-        want_masks=False, n_threads=None, temperature=0.0, top_k=0, top_p=0.0):
+        want_masks=False, n_threads=None, temperature=0.0, top_k=0, top_p=0.0, seq_gamma=None, seq_K=None,
+        seq_p_drop=None):
     """Run the verify step for the listed sequences (all by default).
 
     W: [V, d], h: [B, gamma+1, d] (float32 or uint16 bf16 bits, same dtype);
     draft: int32 [B, gamma]; q_hat: float32 [B, gamma, V] or None;
     modes: uint8 [B].  temperature (0 read as 1) divides every logit row;
-    top_k / top_p (0 = off) process the lossless target.  Returns a dict of
-    numpy arrays whose leading dimension indexes the listed sequences.
+    top_k / top_p (0 = off) process the lossless target.  seq_gamma /
+    seq_K / seq_p_drop ([B] or None) make the batch ragged.  Returns a dict
+    of numpy arrays whose leading dimension indexes the listed sequences.
     """
     W = np.ascontiguousarray(W)
     h = np.ascontiguousarray(h)
@@ -239,11 +242,15 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
             raise ValueError("mask bits need d % 32 == 0")
         out["mask_bits"] = np.zeros((n, T1, K, d // 32), np.uint32)
 
+    rg = None if seq_gamma is None else np.ascontiguousarray(seq_gamma, dtype=np.int32).reshape(B)
+    rk = None if seq_K is None else np.ascontiguousarray(seq_K, dtype=np.int32).reshape(B)
+    rp = None if seq_p_drop is None else np.ascontiguousarray(seq_p_drop, dtype=np.float32).reshape(B)
     prob = _Problem(d=d, vocab=V, batch=B, gamma=G, K=K, dtype=dtype, p_drop=float(p_drop), pad0=0,
                     seed=int(seed) & (2**64 - 1), W=W.ctypes.data, h=h.ctypes.data,
                     draft=_ptr(draft, _c_i32p), q_hat=_ptr(q_hat, _c_f32p), modes=_ptr(modes, _c_u8p),
                     n_seq=n, n_threads=int(n_threads), seq=_ptr(seq, _c_i32p),
-                    temperature=float(temperature), top_k=int(top_k), top_p=float(top_p), pad1=0)
+                    temperature=float(temperature), top_k=int(top_k), top_p=float(top_p), pad1=0,
+                    seq_gamma=_ptr(rg, _c_i32p), seq_K=_ptr(rk, _c_i32p), seq_p_drop=_ptr(rp, _c_f32p))
     res = _Result(**{name: _ptr(out.get(name), ctype) for name, ctype in _Result._fields_})
     rc = lib().dmo_run(ctypes.byref(prob), ctypes.byref(res))
     if rc != 0:

@@ -330,6 +330,12 @@ typedef struct dmo_problem {
     int32_t top_k;         /* lossless rows; 0 = off */
     float top_p;           /* lossless rows; 0 or >= 1 = off */
     uint32_t pad1;
+    /* Ragged batches (NULL = every sequence uses gamma, K, p_drop): sequence
+     * b drafts seq_gamma[b] <= gamma tokens (positions 0..seq_gamma[b]),
+     * lossy sequences use seq_K[b] <= K heads and dropout seq_p_drop[b]. */
+    const int32_t* seq_gamma;
+    const int32_t* seq_K;
+    const float* seq_p_drop;
 } dmo_problem;
 
 typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wanted */
@@ -366,8 +372,6 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
     if (!(P->temperature >= 0.0f) || !(P->top_p >= 0.0f) || P->top_k < 0) return 1;
     /* temperature: the sampled distribution is softmax(l / T) ([PB] Sec. 1) */
     const double temp = P->temperature > 0.0f ? (double)P->temperature : 1.0;
-    const uint32_t thresh = dmo_threshold(P->p_drop);
-    const double pd = (double)P->p_drop;
     const int nthreads = P->n_threads > 0 ? P->n_threads : 1;
 
     double* hm = (double*)malloc(sizeof(double) * (size_t)T1 * K * d);
@@ -392,15 +396,28 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         const int b = P->seq ? P->seq[n] : n;
         const int mode = P->modes[b];
         const int lossy = mode != DMO_LOSSLESS;
+        /* This sequence's drafts, heads and dropout (a ragged batch, [SD]
+         * "Production gotchas", "Batching": sequences keep different numbers
+         * of drafts).  Layout strides stay the batch's gamma and K; the Philox
+         * counters keep pidx = b * (gamma + 1) + t. */
+        const int Gb = P->seq_gamma ? P->seq_gamma[b] : G, Tb = Gb + 1;
+        const int Kb = P->seq_K ? P->seq_K[b] : K;
+        const float pb = P->seq_p_drop ? P->seq_p_drop[b] : P->p_drop;
+        if (Gb < 0 || Gb > G || Kb < 1 || Kb > K || !(pb >= 0.0f && pb < 1.0f)) {
+            free(hm); free(L); free(Lbar); free(prob); free(pproc);
+            free(rmax); free(rlogz); free(rgap); free(rarg); free(clogz); free(cgap); free(carg); free(acc);
+            return 1;
+        }
+        const uint32_t thresh = dmo_threshold(pb);
         /* Lossless sequences verify with the undropped target head, one row
          * per position (reading: the classical test of [SD] / [PB] Sec. 2 is
          * defined for the target's own p). */
-        const int rows = lossy ? K : 1;
+        const int rows = lossy ? Kb : 1;
         /* Inverted-dropout scale 1 / (1 - p_drop), [DM] Eq. (2). */
-        const double scale = lossy ? 1.0 / (1.0 - pd) : 1.0;
+        const double scale = lossy ? 1.0 / (1.0 - (double)pb) : 1.0;
 
         /* [DM] Eq. (1)-(2): masked hidden state per (position, head). */
-        for (int t = 0; t < T1; ++t) {
+        for (int t = 0; t < Tb; ++t) {
             const uint32_t pidx = (uint32_t)(b * T1 + t);
             for (int i = 0; i < rows; ++i) {
                 double* dst = hm + ((size_t)t * K + i) * d;
@@ -423,7 +440,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
 #pragma omp for schedule(static)
             for (int v = 0; v < V; ++v) {
                 for (int j = 0; j < d; ++j) wrow[j] = decode(P->W, P->dtype, (size_t)v * d + j);
-                for (int t = 0; t < T1; ++t) {
+                for (int t = 0; t < Tb; ++t) {
                     for (int i = 0; i < rows; ++i) {
                         const double* x = hm + ((size_t)t * K + i) * d;
                         double s = 0.0;
@@ -436,7 +453,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         }
 
         /* Per-head statistics; centroid l-bar = mean of head logits, [DM] Eq. (5). */
-        for (int t = 0; t < T1; ++t) {
+        for (int t = 0; t < Tb; ++t) {
             for (int i = 0; i < rows; ++i) {
                 const double* l = L + ((size_t)t * K + i) * V;
                 dmo_row_stats(l, V, &rmax[t * K + i], &rlogz[t * K + i], &rarg[t * K + i], &rgap[t * K + i]);
@@ -452,7 +469,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
 
         /* Lossless sequences: the processed target at every position. */
         if (!lossy) {
-            for (int t = 0; t < T1; ++t) {
+            for (int t = 0; t < Tb; ++t) {
                 double lz, mg;
                 int cnt = dmo_processed(L + ((size_t)t * K) * V, V, P->top_k, (double)P->top_p,
                                         pproc + (size_t)t * V, &lz, &mg);
@@ -467,8 +484,8 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
             }
         }
 
-        /* Decisions for every drafted position t < gamma. */
-        for (int t = 0; t < G; ++t) {
+        /* Decisions for every drafted position t < gamma_b. */
+        for (int t = 0; t < Gb; ++t) {
             const int32_t x = P->draft[(size_t)b * G + t];
             const uint32_t pidx = (uint32_t)(b * T1 + t);
             const int valid = x >= 0 && x < V;
@@ -478,7 +495,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
             for (int i = 0; i < rows; ++i)
                 if (rgap[t * K + i] < min_gap) min_gap = rgap[t * K + i];
             if (mode == DMO_NAIVE) {
-                accept = valid && dmo_rule_naive(rarg + t * K, K, x);
+                accept = valid && dmo_rule_naive(rarg + t * K, rows, x);
                 margin = min_gap;
             } else if (mode == DMO_JS) {
                 /* [DM] Algorithm 1: centroid p-bar, head and draft divergences. */
@@ -487,7 +504,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 double* pq = prob + 2 * (size_t)V; /* draft q-hat */
                 for (int v = 0; v < V; ++v) pc[v] = exp(Lbar[(size_t)t * V + v] - clogz[t]);
                 double jmax = -INFINITY;
-                for (int i = 0; i < K; ++i) {
+                for (int i = 0; i < rows; ++i) {
                     const double* l = L + ((size_t)t * K + i) * V;
                     for (int v = 0; v < V; ++v) ph[v] = exp(l[v] - rlogz[t * K + i]);
                     double ji = dmo_js(ph, pc, V);
@@ -498,10 +515,10 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 for (int v = 0; v < V; ++v) pq[v] = (double)q[v];
                 double jq = dmo_js(pq, pc, V);
                 if (R->js_draft) R->js_draft[(size_t)n * G + t] = jq;
-                accept = valid && dmo_rule_js(jq, jmax, rarg + t * K, K, x);
+                accept = valid && dmo_rule_js(jq, jmax, rarg + t * K, rows, x);
                 /* margins of the two branches, for the near-tie accounting */
                 int acc_js = valid && (jq <= jmax);
-                int acc_maj = valid && dmo_rule_js(1.0, 0.0, rarg + t * K, K, x);
+                int acc_maj = valid && dmo_rule_js(1.0, 0.0, rarg + t * K, rows, x);
                 double m_js = fabs(jq - jmax);
                 if (accept)
                     margin = fmax(acc_js ? m_js : 0.0, acc_maj ? min_gap : 0.0);
@@ -527,8 +544,8 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
 
         /* [SD] "The draft-then-verify loop" step 3 / [PB] Sec. 5: scan left to
          * right, the first rejection ends the round. */
-        int A = G;
-        for (int t = 0; t < G; ++t)
+        int A = Gb;
+        for (int t = 0; t < Gb; ++t)
             if (!acc[t]) {
                 A = t;
                 break;
@@ -550,7 +567,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
             double total = 0.0;
             for (int v = 0; v < V; ++v) {
                 double p = pa[v];
-                if (A < G) {
+                if (A < Gb) {
                     double q = (double)P->q_hat[((size_t)b * G + A) * V + v];
                     w[v] = p - q > 0.0 ? p - q : 0.0;
                 } else {
@@ -569,7 +586,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         for (int t = 0; t < T1; ++t) {
             for (int i = 0; i < K; ++i) {
                 size_t o = ((size_t)n * T1 + t) * K + i;
-                int used = i < rows;
+                int used = i < rows && t < Tb;
                 if (R->head_argmax) R->head_argmax[o] = used ? rarg[t * K + i] : -1;
                 if (R->head_gap) R->head_gap[o] = used ? rgap[t * K + i] : NAN;
                 if (R->head_max) R->head_max[o] = used ? rmax[t * K + i] : NAN;
@@ -577,9 +594,9 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
                 if (R->logits && used)
                     memcpy(R->logits + o * V, L + ((size_t)t * K + i) * V, sizeof(double) * V);
             }
-            if (R->centroid_argmax) R->centroid_argmax[(size_t)n * T1 + t] = carg[t];
-            if (R->centroid_gap) R->centroid_gap[(size_t)n * T1 + t] = cgap[t];
-            if (R->centroid_logz) R->centroid_logz[(size_t)n * T1 + t] = clogz[t];
+            if (R->centroid_argmax) R->centroid_argmax[(size_t)n * T1 + t] = t < Tb ? carg[t] : -1;
+            if (R->centroid_gap) R->centroid_gap[(size_t)n * T1 + t] = t < Tb ? cgap[t] : NAN;
+            if (R->centroid_logz) R->centroid_logz[(size_t)n * T1 + t] = t < Tb ? clogz[t] : NAN;
         }
     }
 
