@@ -121,6 +121,19 @@ typedef struct dm_verify_args {
     float top_p;            /* LOSSLESS: of those, keep the tokens whose strictly larger
                                renormalised mass is < top_p; 0 or >= 1 = off */
     uint32_t reserved;      /* 0 */
+    /* Ragged batches ("Speculative Decoding: Draft, Then Verify", "Production
+     * gotchas", "Batching": sequences keep different numbers of drafts).  HOST
+     * arrays of B entries, each NULL = every sequence uses gamma, K, p_drop.
+     * Sequence b verifies positions 0..seq_gamma[b] (its drafts are
+     * draft[b, 0..seq_gamma[b]-1], the rest of its rows unread); a lossy
+     * sequence uses seq_heads[b] of the K heads and dropout seq_p_drop[b].
+     * The layout strides stay gamma and K, and the Philox counters keep
+     * pidx = b * (gamma + 1) + t.  At most 8 distinct seq_p_drop values per
+     * call (else DM_ERR_UNSUPPORTED).  Outputs past a sequence's drafts or
+     * heads are not written (accept_len[b] <= seq_gamma[b]). */
+    const int32_t* seq_gamma;  /* 0 <= seq_gamma[b] <= gamma */
+    const int32_t* seq_heads;  /* 1 <= seq_heads[b] <= K */
+    const float* seq_p_drop;   /* 0 <= seq_p_drop[b] < 1 */
     int32_t* accept_len;    /* device out [B]: A, drafts accepted before the first rejection */
     int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
     /* Optional device outputs for inspection; NULL = not written. */

@@ -41,6 +41,7 @@ class dm_verify_args(ctypes.Structure):
         ("modes", ctypes.c_void_p), ("batch", ctypes.c_int32), ("K", ctypes.c_int32), ("p_drop", ctypes.c_float),
         ("w_layout", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("temperature", ctypes.c_float),
         ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("reserved", ctypes.c_uint32),
+        ("seq_gamma", ctypes.c_void_p), ("seq_heads", ctypes.c_void_p), ("seq_p_drop", ctypes.c_void_p),
         ("accept_len", ctypes.c_void_p),
         ("out_token", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
         ("centroid_argmax", ctypes.c_void_p), ("head_logz", ctypes.c_void_p), ("centroid_logz", ctypes.c_void_p),
@@ -192,7 +193,7 @@ class Verifier:
         return t.data_ptr()
 
     def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, w_layout=DM_W_ROW_MAJOR,
-                  temperature=1.0, top_k=0, top_p=1.0, **debug):
+                  temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None, seq_p_drop=None, **debug):
         import torch
 
         D = self.desc
@@ -224,6 +225,15 @@ class Verifier:
         a.batch, a.K, a.p_drop = B, int(K), float(p_drop)
         a.seed = int(seed) & (2**64 - 1)
         a.temperature, a.top_k, a.top_p = float(temperature), int(top_k), float(top_p)
+        keep = [modes_np]
+        for name, arr, dt in (("seq_gamma", seq_gamma, np.int32), ("seq_heads", seq_heads, np.int32),
+                              ("seq_p_drop", seq_p_drop, np.float32)):
+            if arr is not None:
+                host = np.ascontiguousarray(np.asarray(arr, dtype=dt).reshape(-1))
+                if host.size != B:
+                    raise ValueError(f"{name} must have one entry per sequence")
+                setattr(a, name, host.ctypes.data)
+                keep.append(host)
         a.accept_len = self._expect("accept_len", accept_len, (B,), torch.int32, dev)
         a.out_token = self._expect("out_token", out_token, (B,), torch.int32, dev)
         shapes = {"accept_flags": ((B, G), torch.uint8), "head_argmax": ((B, T1, K), torch.int32),
@@ -238,19 +248,21 @@ class Verifier:
             if t is not None:
                 shp, dt = shapes[name]
                 setattr(a, name, self._expect(name, t, shp, dt, dev))
-        a._keep = (modes_np,)  # keep host memory alive with the struct
+        a._keep = tuple(keep)  # keep host memory alive with the struct
         return a
 
     def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None,
-            w_layout=DM_W_ROW_MAJOR, temperature=1.0, top_k=0, top_p=1.0):
+            w_layout=DM_W_ROW_MAJOR, temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None,
+            seq_p_drop=None):
         """Enqueue one verify step on `stream` (default: torch's current stream).
 
         W is row-major [vocab, d] (w_layout=DM_W_ROW_MAJOR) or the uint8
         buffer pack_w returns (w_layout=DM_W_PANELS).  temperature divides
         every logit row; top_k / top_p (0 / 1 = off) process the lossless
-        target.  Returns a dict with accept_len and out_token (and every debug
-        output when debug=True).  Preallocated outputs can be passed in
-        `outputs`."""
+        target.  seq_gamma / seq_heads / seq_p_drop (host arrays of B, or
+        None) make the batch ragged.  Returns a dict with accept_len and
+        out_token (and every debug output when debug=True).  Preallocated
+        outputs can be passed in `outputs`."""
         import torch
 
         D = self.desc
@@ -275,7 +287,8 @@ class Verifier:
             out.setdefault("filter_logz", torch.full((B, T1), float("nan"), dtype=torch.float32, device=dev))
         dbg = {k: v for k, v in out.items() if k in DEBUG_OUTPUTS}
         args = self.make_args(W, h, draft, q_hat, modes, K, p_drop, seed, out["accept_len"], out["out_token"],
-                              w_layout=w_layout, temperature=temperature, top_k=top_k, top_p=top_p, **dbg)
+                              w_layout=w_layout, temperature=temperature, top_k=top_k, top_p=top_p,
+                              seq_gamma=seq_gamma, seq_heads=seq_heads, seq_p_drop=seq_p_drop, **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         dm_verify_run(self.handle, args, stream)

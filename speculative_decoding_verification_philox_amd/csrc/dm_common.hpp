@@ -11,6 +11,7 @@ namespace dmv {
 constexpr int kMaxBatch = 256;
 constexpr int kMaxK = 16;
 constexpr int kMaskWords = kMaxBatch / 32;
+constexpr int kMaxDropValues = 8;  // distinct per-sequence dropout probabilities in one call
 
 enum Mode : int { kLossless = 0, kNaive = 1, kJs = 2 };
 
@@ -45,6 +46,13 @@ struct Plan {
     float scale_undropped;
     int filter, top_k;
     float top_p;
+    // ragged batches: per-sequence drafts and heads, and the dropout of each
+    // sequence as an index into a small table of (threshold, scale); G, K
+    // above are the largest, which fix the layout
+    int ragged;
+    uint8_t seq_gamma[kMaxBatch], seq_k[kMaxBatch], seq_pi[kMaxBatch];
+    uint32_t p_thresh[kMaxDropValues];
+    float p_scale[kMaxDropValues];
     // slot layout
     int geom, msub, MT, GR, S;
     int ppg;                // lossy positions per group (S / K)
@@ -65,6 +73,18 @@ struct Plan {
     int race_chunks, race_chunk;
     int blk_js, blk_race;
 };
+
+// Per-sequence drafts, heads, dropout threshold and row scale, and the
+// centroid weight 1 / K_b (the same fp32 value everywhere it is used).
+__host__ __device__ inline int seq_G(const Plan& P, int b) { return P.ragged ? P.seq_gamma[b] : P.G; }
+__host__ __device__ inline int seq_K(const Plan& P, int b) { return P.ragged ? P.seq_k[b] : P.K; }
+__host__ __device__ inline uint32_t seq_thresh(const Plan& P, int b) {
+    return P.ragged ? P.p_thresh[P.seq_pi[b]] : P.thresh;
+}
+__host__ __device__ inline float seq_scale(const Plan& P, int b) { return P.ragged ? P.p_scale[P.seq_pi[b]] : P.scale; }
+__host__ __device__ inline float seq_inv_k(const Plan& P, int b) {
+    return P.ragged ? 1.0f / (float)P.seq_k[b] : P.inv_k;
+}
 
 // ------------------------------------------------------------------ layout
 __host__ __device__ inline bool bit_of(const uint32_t* bits, int b) {
@@ -163,6 +183,8 @@ __host__ __device__ inline RowInfo row_info(const Plan& P, int rho) {
         ri.i = lam - slot * P.K;
         ri.lossy = 1;
         ri.lossy_pos = p;
+        // a ragged sequence's rows past its drafts or heads are padding
+        if (P.ragged && (ri.t > P.seq_gamma[ri.b] || ri.i >= P.seq_k[ri.b])) return RowInfo{-1, 0, 0, 0, -1};
     } else {
         int q = ((tile - P.tiles_lossy) * P.GR + g) * P.S + lam;
         if (q >= P.n_lossless_pos) return ri;
@@ -170,6 +192,7 @@ __host__ __device__ inline RowInfo row_info(const Plan& P, int rho) {
         ri.t = q % P.T1;
         ri.i = 0;
         ri.lossy = 0;
+        if (P.ragged && ri.t > P.seq_gamma[ri.b]) return RowInfo{-1, 0, 0, 0, -1};
     }
     return ri;
 }

@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
         RowMeta mt;
         const bool valid = ri.b >= 0;
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
-        mt.scale = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
-        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
+        mt.scale = valid ? (ri.lossy ? seq_scale(P, ri.b) : P.scale_undropped) : 0.0f;
+        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < seq_G(P, ri.b)));
         mt.pad = 0;
         meta[rho] = mt;
     }
@@ -65,13 +65,14 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
     if (ri.b >= 0) {
         if (ri.lossy) {
             const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
+            const uint32_t thr = seq_thresh(P, ri.b);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const u32x4 rr = philox10(u32x4{(uint32_t)(2 * e + q), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
-                bits |= (uint32_t)(rr.x >= P.thresh) << (4 * q);
-                bits |= (uint32_t)(rr.y >= P.thresh) << (4 * q + 1);
-                bits |= (uint32_t)(rr.z >= P.thresh) << (4 * q + 2);
-                bits |= (uint32_t)(rr.w >= P.thresh) << (4 * q + 3);
+                bits |= (uint32_t)(rr.x >= thr) << (4 * q);
+                bits |= (uint32_t)(rr.y >= thr) << (4 * q + 1);
+                bits |= (uint32_t)(rr.z >= thr) << (4 * q + 2);
+                bits |= (uint32_t)(rr.w >= thr) << (4 * q + 3);
             }
         } else {
             bits = 0xffu;
@@ -135,8 +136,8 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
         RowMeta mt;
         const bool valid = ri.b >= 0;
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
-        mt.scale = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
-        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
+        mt.scale = valid ? (ri.lossy ? seq_scale(P, ri.b) : P.scale_undropped) : 0.0f;
+        mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < seq_G(P, ri.b)));
         mt.pad = 0;
         meta[rho] = mt;
     }
@@ -144,14 +145,15 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
     if (ri.b >= 0) {
         if (ri.lossy) {
             const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
+            const uint32_t thr = seq_thresh(P, ri.b);
 #pragma unroll
             for (int qq = 0; qq < EPP / 4; ++qq) {
                 const u32x4 rr =
                     philox10(u32x4{(uint32_t)(e0 / 4 + qq), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
-                bits |= (uint32_t)(rr.x >= P.thresh) << (4 * qq);
-                bits |= (uint32_t)(rr.y >= P.thresh) << (4 * qq + 1);
-                bits |= (uint32_t)(rr.z >= P.thresh) << (4 * qq + 2);
-                bits |= (uint32_t)(rr.w >= P.thresh) << (4 * qq + 3);
+                bits |= (uint32_t)(rr.x >= thr) << (4 * qq);
+                bits |= (uint32_t)(rr.y >= thr) << (4 * qq + 1);
+                bits |= (uint32_t)(rr.z >= thr) << (4 * qq + 2);
+                bits |= (uint32_t)(rr.w >= thr) << (4 * qq + 3);
             }
         } else {
             bits = (1u << EPP) - 1u;
@@ -191,6 +193,14 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ W, u
     v4u x = v4u{0, 0, 0, 0};
     if (row < (size_t)V) x = *(const v4u*)(W + row * row_bytes + (size_t)kb * 64 + (lane >> 4) * 16);
     *(v4u*)(Wp + q * 16) = x;
+}
+
+// Centroid weight of lossy position p: 1 / K_b of its sequence.  Rows of
+// heads past K_b are padding rows whose values are exactly 0, so a sum over
+// all K slots in head order equals the sum over the K_b heads.
+__device__ __forceinline__ float lossy_pos_inv_k(const Plan& P, int p) {
+    if (!P.ragged || p >= P.n_lossy_pos) return P.inv_k;
+    return seq_inv_k(P, select_of(P.lossless_bits, P.B, p / P.T1, false));
 }
 
 // =====================================================================
@@ -380,6 +390,7 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
     if (lossy_tile) {
         for (int slot = 0; slot < P.ppg; ++slot) {
             const int first = slot * P.K;
+            const float inv = lossy_pos_inv_k(P, tile * npt + grp * P.ppg + slot);
             float x[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
                         sum = i == 0 ? v : sum + v;
                     }
                 }
-                x[g] = sum * P.inv_k;
+                x[g] = sum * inv;
             }
             const Stat st = row16_stat<G>(x, ok, col0);
             if (c == 0) s_st[wave][ROWS + grp * P.ppg + slot] = st;
@@ -634,6 +645,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
         if (tile < P.tiles_lossy) {
             for (int slot = 0; slot < P.ppg; ++slot) {
                 const int first = slot * P.K;
+                const float inv = lossy_pos_inv_k(P, tile * (P.GR * P.ppg) + grp * P.ppg + slot);
                 float x[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
                             sum = i == 0 ? v : sum + v;
                         }
                     }
-                    x[g] = sum * P.inv_k;
+                    x[g] = sum * inv;
                 }
                 const Stat st = row16_stat<G>(x, ok, col0);
                 if (c16 == 0) my_st[ROWS + grp * P.ppg + slot] = st;
@@ -740,10 +752,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
     if (threadIdx.x < ROWS) {
         RowInfo ri = row_info(P, tile * ROWS + threadIdx.x);
         bool valid = ri.b >= 0;
-        s_scale[threadIdx.x] = valid ? (ri.lossy ? P.scale : P.scale_undropped) : 0.0f;
+        s_scale[threadIdx.x] = valid ? (ri.lossy ? seq_scale(P, ri.b) : P.scale_undropped) : 0.0f;
         s_canon[threadIdx.x] = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
         s_store[threadIdx.x] =
-            valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < P.G));
+            valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < seq_G(P, ri.b)));
     }
 
     const uint8_t* wp[NS];
@@ -891,7 +903,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
         Stat st = stat_empty();
         if (p < P.n_lossy_pos) {
             for (int c = 0; c < ncol; ++c) {
-                float lb = centroid_logit(P.K, P.inv_k,
+                float lb = centroid_logit(P.K, lossy_pos_inv_k(P, p),
                                           [&](int i) { return et[tile_row(0, g, slot * P.K + i) * PITCH + c]; });
                 stat_push(st, lb, vbase + c);
             }
@@ -948,6 +960,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
         const int p = t - P.R_phys;
         b = select_of(P.lossless_bits, P.B, p / P.T1, false);
         pos_t = p % P.T1;
+        if (pos_t > seq_G(P, b)) return;  // past a ragged sequence's drafts: the whole block leaves
     }
     const Stat* src = part + (size_t)t * P.n_vgroups;
     Stat st = stat_empty();
@@ -1080,6 +1093,9 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     const int jp = blk / P.js_chunks, c = blk - jp * P.js_chunks;
     const int js_rank = jp / G, t = jp - js_rank * G;
     const int b = select_of(P.js_bits, P.B, js_rank, true);
+    if (t >= seq_G(P, b)) return;  // past a ragged sequence's drafts: the whole block leaves
+    const int Kb = seq_K(P, b);    // heads of this sequence (K is the layout stride)
+    const float inv_k = seq_inv_k(P, b);
     const int pidx = b * T1 + t;
     const float* lrow = logits + (size_t)pidx * K * V;
     const float* qrow = q_hat + (size_t)(b * G + t) * V;
@@ -1096,7 +1112,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 v4f x = v4f{0.f, 0.f, 0.f, 0.f};
-                if (i < K) x = *(const v4f*)(lrow + (size_t)i * V + vv);  // K is uniform
+                if (i < Kb) x = *(const v4f*)(lrow + (size_t)i * V + vv);  // Kb is uniform
 #pragma unroll
                 for (int e = 0; e < 4; ++e) l[u + e][i] = ok ? x[e] : 0.0f;
             }
@@ -1112,7 +1128,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 float x = 0.0f;
-                if (i < K) x = lrow[(size_t)i * V + vv];
+                if (i < Kb) x = lrow[(size_t)i * V + vv];
                 l[u][i] = ok ? x : 0.0f;
             }
             const float y = qrow[vv];
@@ -1121,7 +1137,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     }
     float logz[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) logz[i] = i < K ? rowstat[pidx * K + i].logz : 0.0f;
+    for (int i = 0; i < KMAX; ++i) logz[i] = i < Kb ? rowstat[pidx * K + i].logz : 0.0f;
     const float logz_c = centstat[pidx].logz;
 
     float acc[KMAX + 1];
@@ -1135,12 +1151,12 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
         float lsum = l[u][0];
 #pragma unroll
         for (int i = 1; i < KMAX; ++i)
-            if (i < K) lsum += l[u][i];
-        const float bb = lsum * P.inv_k - logz_c;
+            if (i < Kb) lsum += l[u][i];
+        const float bb = lsum * inv_k - logz_c;
         const float pb = hw_exp(bb) * live;
 #pragma unroll
         for (int i = 0; i < KMAX; ++i)
-            if (i < K) {
+            if (i < Kb) {
                 const float a = l[u][i] - logz[i];
                 acc[i] += js_entry(a, hw_exp(a) * live, bb, pb);
             }
@@ -1149,12 +1165,12 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     }
 #pragma unroll
     for (int i = 0; i <= KMAX; ++i)
-        if (i < K || i == KMAX) {
+        if (i < Kb || i == KMAX) {
             const float x = wave_sum(acc[i]);
             if (lane == 0) s_red[wave][i == KMAX ? kMaxK : i] = x;
         }
     __syncthreads();
-    if (threadIdx.x <= K) {
+    if ((int)threadIdx.x < Kb || (int)threadIdx.x == K) {  // heads, then the draft in slot K
         const int i = threadIdx.x == K ? kMaxK : threadIdx.x;
         float x = 0.0f;
 #pragma unroll
@@ -1185,9 +1201,10 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 
     const int r = blk / P.race_chunks, c = blk - r * P.race_chunks;
     const int b = select_of(P.lossless_bits, P.B, r, true);
+    const int Gb = seq_G(P, b);
     if (wave == 0) {
-        const bool reject = lane < G && !lossless_accept(P, b, lane, draft, q_hat, logits, rowstat, filt);
-        const int A = first_reject(reject, G);
+        const bool reject = lane < Gb && !lossless_accept(P, b, lane, draft, q_hat, logits, rowstat, filt);
+        const int A = first_reject(reject, Gb);
         if (lane == 0) s_A = A;
     }
     __syncthreads();
@@ -1200,7 +1217,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
         thresh = f.thresh;
     }
     const float* lrow = logits + (size_t)pidx * K * V;
-    const float* qrow = A < G ? q_hat + (size_t)(b * G + A) * V : nullptr;
+    const float* qrow = A < Gb ? q_hat + (size_t)(b * G + A) * V : nullptr;
     unsigned long long best_r = 0ull, best_p = 0ull;
     const int v0 = c * P.race_chunk;
     const int v1 = min(v0 + P.race_chunk, V);
@@ -1271,7 +1288,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                                                            float* __restrict__ dbg_js_draft) {
     __shared__ float s_js[32][kMaxK + 1];
     const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int K = P.K, G = P.G, T1 = P.T1;
+    const int K = P.K, G = P.G, T1 = P.T1;  // layout strides
+    const int Gb = seq_G(P, b), Kb = seq_K(P, b);  // this sequence's drafts and heads
     const bool lossless = bit_of(P.lossless_bits, b);
     const bool js = bit_of(P.js_bits, b);
 
@@ -1282,13 +1300,13 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
     for (int i = 0; i < kMaxK; ++i) head_idx[i] = -1;
     unsigned long long best_r = 0ull, best_p = 0ull;
     if (wave == 0) {
-        if (lane < G) x = draft[b * G + lane];
+        if (lane < Gb) x = draft[b * G + lane];
         if (!lossless) {
-            if (lane <= G) cent_idx = centstat[b * T1 + lane].idx;
-            if (lane < G) {
+            if (lane <= Gb) cent_idx = centstat[b * T1 + lane].idx;
+            if (lane < Gb) {
 #pragma unroll
                 for (int i = 0; i < kMaxK; ++i)
-                    if (i < K) head_idx[i] = rowstat[(b * T1 + lane) * K + i].idx;
+                    if (i < Kb) head_idx[i] = rowstat[(b * T1 + lane) * K + i].idx;
             }
         } else if (lane == 0) {
             best_r = race_best[2 * b];
@@ -1326,29 +1344,29 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
     __syncthreads();
     if (wave != 0) return;
     bool accept = false;
-    if (lane < G) {
+    if (lane < Gb) {
         if (lossless) {
             accept = lossless_accept(P, b, lane, draft, q_hat, logits, rowstat, filt);
         } else {
             int count = 0;
 #pragma unroll
-            for (int i = 0; i < kMaxK; ++i) count += (i < K && head_idx[i] == x) ? 1 : 0;
+            for (int i = 0; i < kMaxK; ++i) count += (i < Kb && head_idx[i] == x) ? 1 : 0;
             const bool valid = x >= 0 && x < P.V;
             if (js) {
                 float jmax = -INFINITY;
-                for (int i = 0; i < K; ++i) jmax = fmaxf(jmax, s_js[lane][i]);
+                for (int i = 0; i < Kb; ++i) jmax = fmaxf(jmax, s_js[lane][i]);
                 const float jq = s_js[lane][K];
-                accept = valid && (jq <= jmax || 2 * count > K);  // Algorithm 1: Eq. (6), else Eq. (7)
+                accept = valid && (jq <= jmax || 2 * count > Kb);  // Algorithm 1: Eq. (6), else Eq. (7)
                 if (dbg_js_draft) dbg_js_draft[b * G + lane] = jq;
                 if (dbg_js_heads)
-                    for (int i = 0; i < K; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
+                    for (int i = 0; i < Kb; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
             } else {
                 accept = valid && count > 0;  // DropMatch Eq. (4)
             }
         }
         if (dbg_flags) dbg_flags[b * G + lane] = accept ? 1 : 0;
     }
-    const int A = first_reject(lane < G && !accept, G);
+    const int A = first_reject(lane < Gb && !accept, Gb);
     const int token_lossy = __shfl(cent_idx, A, 64);  // greedy on the centroid at A
     if (lane == 0) {
         accept_len[b] = A;
@@ -1676,6 +1694,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(const Plan P, const f
     __shared__ FilterLds L;
     const int r = blockIdx.x / P.T1, t = blockIdx.x - r * P.T1;
     const int b = select_of(P.lossless_bits, P.B, r, true);
+    if (t > seq_G(P, b)) return;  // past a ragged sequence's drafts: the whole block leaves
     const int pidx = b * P.T1 + t;
     const float* row = logits + (size_t)pidx * P.K * P.V;
     const RowStat rs = rowstat[pidx * P.K];

@@ -71,6 +71,21 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
         uint8_t m = a->modes[b];
         if (m > DM_MODE_JS_MAJORITY) return DM_ERR_INVALID_ARGUMENT;
         if (m != DM_MODE_NAIVE) need_q = true;
+        if (a->seq_gamma && (a->seq_gamma[b] < 0 || a->seq_gamma[b] > D->gamma)) return DM_ERR_INVALID_ARGUMENT;
+        if (a->seq_heads && (a->seq_heads[b] < 1 || a->seq_heads[b] > a->K)) return DM_ERR_INVALID_ARGUMENT;
+        if (a->seq_p_drop && !(a->seq_p_drop[b] >= 0.0f && a->seq_p_drop[b] < 1.0f)) return DM_ERR_INVALID_ARGUMENT;
+    }
+    if (a->seq_p_drop) {
+        float seen[kMaxDropValues];
+        int n = 0;
+        for (int b = 0; b < a->batch; ++b) {
+            int k = 0;
+            while (k < n && seen[k] != a->seq_p_drop[b]) ++k;
+            if (k == n) {
+                if (n == kMaxDropValues) return DM_ERR_UNSUPPORTED;
+                seen[n++] = a->seq_p_drop[b];
+            }
+        }
     }
     if (need_q && D->gamma > 0 && !a->q_hat) return DM_ERR_INVALID_ARGUMENT;
     if (!aligned(a->W, 16) || !aligned(a->h, 16)) return DM_ERR_UNSUPPORTED;
@@ -368,6 +383,25 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     P.scale_undropped = (float)(1.0 / temp);
     P.top_k = a->top_k;
     P.top_p = a->top_p;
+    // ragged batches: per-sequence drafts and heads, dropout by palette index
+    P.ragged = a->seq_gamma || a->seq_heads || a->seq_p_drop;
+    if (P.ragged) {
+        int n_p = 0;
+        float pal[kMaxDropValues];
+        for (int b = 0; b < a->batch; ++b) {
+            P.seq_gamma[b] = (uint8_t)(a->seq_gamma ? a->seq_gamma[b] : D.gamma);
+            P.seq_k[b] = (uint8_t)(a->seq_heads ? a->seq_heads[b] : a->K);
+            const float pb = a->seq_p_drop ? a->seq_p_drop[b] : a->p_drop;
+            int k = 0;
+            while (k < n_p && pal[k] != pb) ++k;
+            if (k == n_p) {  // at most kMaxDropValues: checked above
+                pal[n_p++] = pb;
+                P.p_thresh[k] = drop_threshold(pb);
+                P.p_scale[k] = (float)(1.0 / ((1.0 - (double)pb) * temp));
+            }
+            P.seq_pi[b] = (uint8_t)k;
+        }
+    }
     P.filter = n_lossless > 0 && ((a->top_k > 0 && a->top_k < D.vocab) || (a->top_p > 0.0f && a->top_p < 1.0f));
     P.inv_k = 1.0f / (float)a->K;
     P.thresh = drop_threshold(a->p_drop);
@@ -394,6 +428,7 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
         if (e != hipSuccess) return DM_ERR_HIP; \
     } while (0)
     if (a->head_argmax) DM_TRY(launch_fill_i32(a->head_argmax, a->batch * T1 * a->K, -1, st));
+    if (a->centroid_argmax && P.ragged) DM_TRY(launch_fill_i32(a->centroid_argmax, a->batch * T1, -1, st));
     if (a->mask_bits) DM_TRY(launch_fill_i32((int32_t*)a->mask_bits, a->batch * T1 * a->K * (D.d / 32), 0, st));
     DM_TRY(launch_prep(P, a->h, h->Hm, h->meta, a->mask_bits, st));
     const bool prof = h->prof_start && h->prof_stop;

@@ -96,11 +96,12 @@ def weights(ver, inp: Inputs, layout):
     return inp.W
 
 
-def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None):
+def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None, ragged=None):
+    """`ragged`: dict of seq_gamma / seq_heads / seq_p_drop host arrays."""
     import torch
 
     out = ver.run(weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug,
-                  w_layout=layout, **(sampling or {}))
+                  w_layout=layout, **(sampling or {}), **(ragged or {}))
     torch.cuda.synchronize()
     res = {}
     for k, v in out.items():
@@ -132,69 +133,77 @@ class Report:
             setattr(self, f.name, max(a, b) if f.name.startswith("max_") else a + b)
 
 
-def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False) -> Report:
+def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False, ragged=None) -> Report:
     """Assert the parity bar; returns the near-tie accounting.  `seqs` are the
     batch indices the oracle evaluated (its rows, in order).  `filtered`: a
-    top-k / top-p filter was on."""
+    top-k / top-p filter was on.  `ragged`: the per-sequence arrays; each
+    sequence is compared on its own positions and heads."""
     modes = np.asarray(modes)
     n = ora["accept_len"].shape[0]
     seqs = np.arange(n) if seqs is None else np.asarray(seqs)
     rep = Report()
-    G = ora["accept_flags"].shape[1]
+    G_all = ora["accept_flags"].shape[1]
+    ragged = ragged or {}
     for r, b in enumerate(seqs):
         mode = int(modes[b])
-        rows = K if mode != wl.LOSSLESS else 1
+        G = int(ragged["seq_gamma"][b]) if ragged.get("seq_gamma") is not None else G_all
+        Kb = int(ragged["seq_heads"][b]) if ragged.get("seq_heads") is not None else K
+        T = G + 1
+        rows = Kb if mode != wl.LOSSLESS else 1
         fnear = np.zeros(G + 1, bool)
         if filtered and mode == wl.LOSSLESS:
-            fnear = ora["filter_margin"][r] < FILTER_MARGIN
+            fnear = ora["filter_margin"][r][:T] < FILTER_MARGIN
             rep.filter_positions += G + 1
             rep.filter_near_ties += int(fnear.sum())
             if "filter_count" in gpu:
-                gcnt, ocnt = gpu["filter_count"][b], ora["filter_count"][r]
+                gcnt, ocnt = gpu["filter_count"][b][:T], ora["filter_count"][r][:T]
                 bad = gcnt != ocnt
                 assert np.all(fnear[bad]), (
                     f"kept-set size of sequence {b}: gpu {gcnt[bad & ~fnear]} oracle {ocnt[bad & ~fnear]}")
                 same = ~bad
-                lz = np.abs(gpu["filter_logz"][b][same] - ora["filter_logz"][r][same])
+                lz = np.abs(gpu["filter_logz"][b][:T][same] - ora["filter_logz"][r][:T][same])
                 lz = float(lz.max()) if lz.size else 0.0
                 rep.max_logz_err = max(rep.max_logz_err, lz)
                 assert lz <= LOGZ_TOL, f"kept-set log normaliser of sequence {b} off by {lz}"
         if check_debug:
             if "mask_bits" in gpu and "mask_bits" in ora:
-                np.testing.assert_array_equal(gpu["mask_bits"][b, :, :rows], ora["mask_bits"][r, :, :rows],
+                np.testing.assert_array_equal(gpu["mask_bits"][b, :T, :rows], ora["mask_bits"][r, :T, :rows],
                                               err_msg=f"mask bits of sequence {b}")
             if "logits" in gpu and "logits" in ora:
-                err = np.abs(gpu["logits"][b, :, :rows].astype(np.float64) - ora["logits"][r, :, :rows]).max()
+                err = np.abs(gpu["logits"][b, :T, :rows].astype(np.float64) - ora["logits"][r, :T, :rows]).max()
                 rep.max_logit_err = max(rep.max_logit_err, float(err))
                 assert err <= LOGIT_TOL, f"logits of sequence {b} off by {err}"
-            lz = np.abs(gpu["head_logz"][b, :, :rows] - ora["head_logz"][r, :, :rows]).max()
+            lz = np.abs(gpu["head_logz"][b, :T, :rows] - ora["head_logz"][r, :T, :rows]).max()
             rep.max_logz_err = max(rep.max_logz_err, float(lz))
             assert lz <= LOGZ_TOL, f"log-partition of sequence {b} off by {lz}"
-            ga, oa, gap = gpu["head_argmax"][b, :, :rows], ora["head_argmax"][r, :, :rows], ora["head_gap"][r, :, :rows]
+            ga, oa, gap = (gpu["head_argmax"][b, :T, :rows], ora["head_argmax"][r, :T, :rows],
+                           ora["head_gap"][r, :T, :rows])
             bad = ga != oa
             rep.argmax_rows += ga.size
             assert np.all(gap[bad] < MARGIN), f"head argmax mismatch of sequence {b} at gaps {gap[bad]}"
             rep.argmax_near_tie_mismatch += int(bad.sum())
             if rows < K:
                 assert np.all(gpu["head_argmax"][b, :, rows:] == -1)
-            gc, oc, cgap = gpu["centroid_argmax"][b], ora["centroid_argmax"][r], ora["centroid_gap"][r]
+            assert np.all(gpu["head_argmax"][b, T:] == -1), f"head argmax written past the drafts of sequence {b}"
+            gc, oc, cgap = gpu["centroid_argmax"][b][:T], ora["centroid_argmax"][r][:T], ora["centroid_gap"][r][:T]
             bad = gc != oc
             rep.argmax_rows += gc.size
             assert np.all(cgap[bad] < MARGIN), f"centroid argmax mismatch of sequence {b} at gaps {cgap[bad]}"
             rep.argmax_near_tie_mismatch += int(bad.sum())
             if mode == wl.JS and G > 0:
-                e1 = np.abs(gpu["js_heads"][b] - ora["js_heads"][r]).max()
-                e2 = np.abs(gpu["js_draft"][b] - ora["js_draft"][r]).max()
+                e1 = np.abs(gpu["js_heads"][b, :G, :rows] - ora["js_heads"][r, :G, :rows]).max()
+                e2 = np.abs(gpu["js_draft"][b, :G] - ora["js_draft"][r, :G]).max()
                 rep.max_js_err = max(rep.max_js_err, float(e1), float(e2))
                 assert max(e1, e2) <= JS_TOL, f"JS of sequence {b} off by {max(e1, e2)}"
         # decisions
-        margin = ora["margin"][r]
+        margin = ora["margin"][r][:G]
         near = (margin < MARGIN) | fnear[:G]
         rep.decisions += G
         rep.decision_near_ties += int(near.sum())
         if "accept_flags" in gpu:
-            gf = gpu["accept_flags"][b].astype(bool)
-            of = ora["accept_flags"][r].astype(bool)
+            assert not gpu["accept_flags"][b][G:].any(), f"decisions written past the drafts of sequence {b}"
+            gf = gpu["accept_flags"][b][:G].astype(bool)
+            of = ora["accept_flags"][r][:G].astype(bool)
             bad = gf != of
             assert np.all(near[bad]), f"decision mismatch of sequence {b} at positions {np.nonzero(bad & ~near)[0]}"
             rep.decision_mismatch_exempt += int(bad.sum())
@@ -215,6 +224,9 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False) -> 
     return rep
 
 
-def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None):
+def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None, ragged=None):
+    rg = dict(ragged or {})
+    if "seq_heads" in rg:
+        rg["seq_K"] = rg.pop("seq_heads")
     return oracle.run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=seqs, want_logits=debug,
-                      want_masks=debug and W.shape[1] % 32 == 0, **(sampling or {}))
+                      want_masks=debug and W.shape[1] % 32 == 0, **(sampling or {}), **rg)

@@ -48,9 +48,10 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header(lib):
     # sizes follow from the field lists in include/dm_verify.h on LP64
     assert ctypes.sizeof(B.dm_verify_desc) == 24
-    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 2 * 8 + 11 * 8
+    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 3 * 8 + 2 * 8 + 11 * 8
     assert B.dm_verify_args.seed.offset == 56
-    assert B.dm_verify_args.temperature.offset == 64 and B.dm_verify_args.accept_len.offset == 80
+    assert B.dm_verify_args.temperature.offset == 64 and B.dm_verify_args.seq_gamma.offset == 80
+    assert B.dm_verify_args.accept_len.offset == 104
 
 
 def desc(**kw):
@@ -67,9 +68,14 @@ def args(B_=2, K=5, modes=(B.DM_MODE_JS_MAJORITY, B.DM_MODE_NAIVE), **kw):
     a.modes = modes_np.ctypes.data if modes is not None else None
     a.batch, a.K, a.p_drop, a.w_layout, a.seed = B_, K, 0.2, 0, 7
     a.accept_len = a.out_token = fake
+    keep = [modes_np]
     for k, v in kw.items():
+        if k in ("seq_gamma", "seq_heads", "seq_p_drop"):  # host arrays
+            arr = np.ascontiguousarray(v, dtype=np.float32 if k == "seq_p_drop" else np.int32)
+            keep.append(arr)
+            v = arr.ctypes.data
         setattr(a, k, v)
-    a._modes = modes_np
+    a._modes = keep
     return a
 
 
@@ -127,9 +133,28 @@ def test_bad_desc(lib, field, value, status):
     (dict(top_p=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
     (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
     (dict(filter_count=0x10002), B.DM_ERR_UNSUPPORTED),
+    (dict(seq_gamma=[5, 0]), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(seq_gamma=[-1, 0]), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(seq_heads=[0, 5]), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(seq_heads=[6, 5]), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(seq_p_drop=[1.0, 0.1]), B.DM_ERR_INVALID_ARGUMENT),
+    (dict(seq_p_drop=[float("nan"), 0.1]), B.DM_ERR_INVALID_ARGUMENT),
 ])
 def test_bad_args(lib, change, status):
     assert B.dm_verify_check(desc(), args(**change)) == status
+
+
+def test_ragged_settings_in_range_pass(lib):
+    assert B.dm_verify_check(desc(), args(seq_gamma=[4, 0], seq_heads=[5, 1], seq_p_drop=[0.0, 0.9])) == B.DM_OK
+
+
+def test_more_than_eight_dropout_values_are_unsupported(lib):
+    modes = (B.DM_MODE_NAIVE,) * 8
+    d = desc(max_batch=9)
+    assert B.dm_verify_check(d, args(B_=8, modes=modes, seq_p_drop=[0.1 * i for i in range(8)])) == B.DM_OK
+    modes9 = (B.DM_MODE_NAIVE,) * 9
+    assert B.dm_verify_check(d, args(B_=9, modes=modes9,
+                                     seq_p_drop=[0.05 * i for i in range(9)])) == B.DM_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("change", [dict(temperature=0.0), dict(temperature=0.7), dict(temperature=3.0),

@@ -20,7 +20,8 @@ def layout(request):
     return request.param
 
 
-def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None, layout=P.ROW_MAJOR, sampling=None):
+def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None, layout=P.ROW_MAJOR, sampling=None,
+           ragged=None):
     ver = P.make_verifier(W, h, K, max_batch)
     inp = P.Inputs(W, h, draft, q)
     rep = P.Report()
@@ -29,9 +30,9 @@ def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None, layo
     for seed in seeds:
         print(f"  seed={seed} B={h.shape[0]} K={K} p={p} modes={np.bincount(modes, minlength=3)} layout={layout}"
               f" sampling={smp}", flush=True)
-        g = P.run_gpu(ver, inp, modes, K, p, seed, layout=layout, sampling=sampling)
-        o = P.oracle_run(W, h, draft, q, modes, K, p, seed, sampling=sampling)
-        rep.add(P.compare(g, o, modes, K, filtered=filtered))
+        g = P.run_gpu(ver, inp, modes, K, p, seed, layout=layout, sampling=sampling, ragged=ragged)
+        o = P.oracle_run(W, h, draft, q, modes, K, p, seed, sampling=sampling, ragged=ragged)
+        rep.add(P.compare(g, o, modes, K, filtered=filtered, ragged=ragged))
     ver.close()
     print(rep, flush=True)
     if report is not None:
