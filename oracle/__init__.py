@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dm_oracle.c")
 _LIB = os.path.join(_HERE, "libdmoracle.so")
 
-LOSSLESS, NAIVE, JS = 0, 1, 2
+LOSSLESS, NAIVE, JS, TREE_NAIVE = 0, 1, 2, 3
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_u8p = ctypes.POINTER(ctypes.c_uint8)
@@ -38,7 +38,7 @@ class _Problem(ctypes.Structure):
         ("q_hat", _c_f32p), ("modes", _c_u8p), ("n_seq", ctypes.c_int32),
         ("n_threads", ctypes.c_int32), ("seq", _c_i32p), ("temperature", ctypes.c_float),
         ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("pad1", ctypes.c_uint32),
-        ("seq_gamma", _c_i32p), ("seq_K", _c_i32p), ("seq_p_drop", _c_f32p),
+        ("seq_gamma", _c_i32p), ("seq_K", _c_i32p), ("seq_p_drop", _c_f32p), ("tree_parent", _c_i32p),
     ]
 
 
@@ -50,7 +50,7 @@ class _Result(ctypes.Structure):
         ("centroid_argmax", _c_i32p), ("centroid_gap", _c_f64p), ("centroid_logz", _c_f64p),
         ("js_heads", _c_f64p), ("js_draft", _c_f64p), ("logits", _c_f64p),
         ("mask_bits", _c_u32p), ("race_gap", _c_f64p), ("filter_count", _c_i32p),
-        ("filter_logz", _c_f64p), ("filter_margin", _c_f64p),
+        ("filter_logz", _c_f64p), ("filter_margin", _c_f64p), ("accept_pos", _c_i32p),
     ]
 
 
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.dmo_processed.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f64p, _c_f64p,
                                     _c_f64p]
         L.dmo_processed.restype = ctypes.c_int
+        L.dmo_tree_walk.argtypes = [_c_i32p, _c_u8p, ctypes.c_int, _c_i32p]
+        L.dmo_tree_walk.restype = ctypes.c_int
         L.dmo_run.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Result)]
         L.dmo_run.restype = ctypes.c_int
         _lib = L
@@ -177,17 +179,32 @@ def processed(l, top_k=0, top_p=0.0):
     return p, int(cnt), lz.value, mg.value
 
 
+def tree_walk(parent, flags):
+    """The round on a token tree (see dmo_tree_walk): (depth of the deepest
+    accepted path, position of its last node)."""
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    fl = np.ascontiguousarray(flags, dtype=np.uint8)
+    assert par.shape == fl.shape and par.ndim == 1
+    pos = ctypes.c_int32()
+    depth = lib().dmo_tree_walk(_ptr(par, _c_i32p), _ptr(fl, _c_u8p), par.size, ctypes.byref(pos))
+    if depth < 0:
+        raise MemoryError("dmo_tree_walk")
+    return int(depth), int(pos.value)
+
+
 # -------------------------------------------------------------- full verify
 def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False,
         want_masks=False, n_threads=None, temperature=0.0, top_k=0, top_p=0.0, seq_gamma=None, seq_K=None,
-        seq_p_drop=None):
+        seq_p_drop=None, tree_parent=None):
     """Run the verify step for the listed sequences (all by default).
 
     W: [V, d], h: [B, gamma+1, d] (float32 or uint16 bf16 bits, same dtype);
     draft: int32 [B, gamma]; q_hat: float32 [B, gamma, V] or None;
     modes: uint8 [B].  temperature (0 read as 1) divides every logit row;
     top_k / top_p (0 = off) process the lossless target.  seq_gamma /
-    seq_K / seq_p_drop ([B] or None) make the batch ragged.  Returns a dict
+    seq_K / seq_p_drop ([B] or None) make the batch ragged.  tree_parent
+    (int32 [B, gamma]) gives the parent position of every draft of the
+    TREE_NAIVE sequences (a chain is parent[t] = t).  Returns a dict
     of numpy arrays whose leading dimension indexes the listed sequences.
     """
     W = np.ascontiguousarray(W)
@@ -208,7 +225,7 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
     modes = np.ascontiguousarray(modes, dtype=np.uint8).reshape(B)
     if q_hat is not None:
         q_hat = np.ascontiguousarray(q_hat, dtype=np.float32).reshape(B, G, V)
-    elif np.any(modes != NAIVE):
+    elif np.any((modes != NAIVE) & (modes != TREE_NAIVE)):
         raise ValueError("q_hat is required when a sequence uses the JS or lossless rule")
     seq = np.arange(B, dtype=np.int32) if seqs is None else np.ascontiguousarray(seqs, dtype=np.int32)
     n = seq.size
@@ -217,6 +234,7 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
 
     out = {
         "accept_len": np.full(n, -1, np.int32),
+        "accept_pos": np.full(n, -1, np.int32),
         "out_token": np.full(n, -1, np.int32),
         "accept_flags": np.zeros((n, G), np.uint8),
         "margin": np.full((n, G), np.nan),
@@ -245,12 +263,14 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
     rg = None if seq_gamma is None else np.ascontiguousarray(seq_gamma, dtype=np.int32).reshape(B)
     rk = None if seq_K is None else np.ascontiguousarray(seq_K, dtype=np.int32).reshape(B)
     rp = None if seq_p_drop is None else np.ascontiguousarray(seq_p_drop, dtype=np.float32).reshape(B)
+    tp = None if tree_parent is None else np.ascontiguousarray(tree_parent, dtype=np.int32).reshape(B, G)
     prob = _Problem(d=d, vocab=V, batch=B, gamma=G, K=K, dtype=dtype, p_drop=float(p_drop), pad0=0,
                     seed=int(seed) & (2**64 - 1), W=W.ctypes.data, h=h.ctypes.data,
                     draft=_ptr(draft, _c_i32p), q_hat=_ptr(q_hat, _c_f32p), modes=_ptr(modes, _c_u8p),
                     n_seq=n, n_threads=int(n_threads), seq=_ptr(seq, _c_i32p),
                     temperature=float(temperature), top_k=int(top_k), top_p=float(top_p), pad1=0,
-                    seq_gamma=_ptr(rg, _c_i32p), seq_K=_ptr(rk, _c_i32p), seq_p_drop=_ptr(rp, _c_f32p))
+                    seq_gamma=_ptr(rg, _c_i32p), seq_K=_ptr(rk, _c_i32p), seq_p_drop=_ptr(rp, _c_f32p),
+                    tree_parent=_ptr(tp, _c_i32p))
     res = _Result(**{name: _ptr(out.get(name), ctype) for name, ctype in _Result._fields_})
     rc = lib().dmo_run(ctypes.byref(prob), ctypes.byref(res))
     if rc != 0:

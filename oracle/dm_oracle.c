@@ -17,6 +17,10 @@
  *   [PB]  "Why speculative decoding preserves distributions but may not be
  *         faster" (youchengli.com, probability budget): Sec. 1, Sec. 2, Sec. 5
  *         (verify-round pseudocode).
+ *   [TR]  "Speculative Decoding: Draft, Then Verify", "Variants": one
+ *         target pass verifies a tree of candidate continuations under a
+ *         tree-shaped attention mask (Medusa, EAGLE); [DM] Sec. 4.4: on
+ *         EAGLE3's trees the naive rule, Eq. (4), is the one applied.
  *   [PX]  Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *         1, 2, 3" (SC'11): the Philox4x32-10 counter-based generator.
  *
@@ -34,6 +38,7 @@
 #define DMO_LOSSLESS 0
 #define DMO_NAIVE 1
 #define DMO_JS 2
+#define DMO_TREE_NAIVE 3
 
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 [PX]: ten rounds of the Philox S-box on a 128-bit counter,  */
@@ -309,6 +314,46 @@ int dmo_rule_lossless(double u, double px, double qx)
     return u * qx < px;
 }
 
+/* [TR] with [DM] Sec. 4.4: the round on a token tree.  Node t+1 holds draft
+ * t and hangs below position parent[t] (0 = the root); flags[t] is the rule's
+ * decision for draft t at its parent.  A node is on an accepted path iff it
+ * passed and so did every node between it and the root; the round commits
+ * the deepest such path (reading: on equal depths the node that comes first,
+ * the smallest index), then the target's token at its last node.  A parent
+ * outside [0, t] puts the node off every path.  Returns the depth (drafts
+ * committed) and writes the last node's position (0 = the root) to *pos. */
+int dmo_tree_walk(const int32_t* parent, const uint8_t* flags, int G, int32_t* pos)
+{
+    int32_t* depth = (int32_t*)malloc(sizeof(int32_t) * (size_t)(G + 1));
+    uint8_t* on_path = (uint8_t*)malloc((size_t)(G + 1));
+    if (!depth || !on_path) {
+        free(depth);
+        free(on_path);
+        return -1;
+    }
+    depth[0] = 0;
+    on_path[0] = 1; /* the root is committed already */
+    int best = 0, best_pos = 0;
+    for (int t = 0; t < G; ++t) {
+        const int node = t + 1, up = parent[t];
+        if (up < 0 || up > t) {
+            depth[node] = 0;
+            on_path[node] = 0;
+            continue;
+        }
+        depth[node] = depth[up] + 1;
+        on_path[node] = flags[t] && on_path[up];
+        if (on_path[node] && depth[node] > best) {
+            best = depth[node];
+            best_pos = node;
+        }
+    }
+    free(depth);
+    free(on_path);
+    *pos = best_pos;
+    return best;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Problem / result records (this library's own layout).                     */
 /* ------------------------------------------------------------------------ */
@@ -336,6 +381,12 @@ typedef struct dmo_problem {
     const int32_t* seq_gamma;
     const int32_t* seq_K;
     const float* seq_p_drop;
+    /* Token trees (NULL = every sequence is a chain): for a DMO_TREE_NAIVE
+     * sequence, draft t is node t+1 and tree_parent[b, t] in [0, t] is the
+     * position whose hidden state predicts it (0 = the root, the last
+     * committed token); h[b, t+1] is the state after the root-to-node path.
+     * A chain is tree_parent[b, t] = t. */
+    const int32_t* tree_parent;
 } dmo_problem;
 
 typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wanted */
@@ -359,6 +410,7 @@ typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wa
     int32_t* filter_count;    /* [n, gamma+1] lossless sequences: |S| of the processed target */
     double* filter_logz;      /* [n, gamma+1] lossless sequences: log sum over S of e^l */
     double* filter_margin;    /* [n, gamma+1] lossless sequences: see dmo_processed */
+    int32_t* accept_pos;      /* [n] position of the last kept node (chains: accept_len) */
 } dmo_result;
 
 /* ------------------------------------------------------------------------ */
@@ -396,6 +448,11 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         const int b = P->seq ? P->seq[n] : n;
         const int mode = P->modes[b];
         const int lossy = mode != DMO_LOSSLESS;
+        if (mode > DMO_TREE_NAIVE || (mode == DMO_TREE_NAIVE && G > 0 && !P->tree_parent)) {
+            free(hm); free(L); free(Lbar); free(prob); free(pproc);
+            free(rmax); free(rlogz); free(rgap); free(rarg); free(clogz); free(cgap); free(carg); free(acc);
+            return 1;
+        }
         /* This sequence's drafts, heads and dropout (a ragged batch, [SD]
          * "Production gotchas", "Batching": sequences keep different numbers
          * of drafts).  Layout strides stay the batch's gamma and K; the Philox
@@ -497,6 +554,15 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
             if (mode == DMO_NAIVE) {
                 accept = valid && dmo_rule_naive(rarg + t * K, rows, x);
                 margin = min_gap;
+            } else if (mode == DMO_TREE_NAIVE) {
+                /* [TR]: draft t is judged by the heads at its parent position */
+                const int32_t up = P->tree_parent[(size_t)b * G + t];
+                if (up >= 0 && up <= t) {
+                    accept = valid && dmo_rule_naive(rarg + up * K, rows, x);
+                    margin = INFINITY;
+                    for (int i = 0; i < rows; ++i)
+                        if (rgap[up * K + i] < margin) margin = rgap[up * K + i];
+                }
             } else if (mode == DMO_JS) {
                 /* [DM] Algorithm 1: centroid p-bar, head and draft divergences. */
                 double* pc = prob;                 /* centroid p-bar */
@@ -543,21 +609,34 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         }
 
         /* [SD] "The draft-then-verify loop" step 3 / [PB] Sec. 5: scan left to
-         * right, the first rejection ends the round. */
+         * right, the first rejection ends the round.  A tree keeps its
+         * deepest accepted path instead, and emits at that path's end. */
         int A = Gb;
-        for (int t = 0; t < Gb; ++t)
-            if (!acc[t]) {
-                A = t;
-                break;
+        int32_t pos = Gb;
+        if (mode == DMO_TREE_NAIVE) {
+            A = dmo_tree_walk(P->tree_parent + (size_t)b * G, acc, Gb, &pos);
+            if (A < 0) {
+                free(hm); free(L); free(Lbar); free(prob); free(pproc);
+                free(rmax); free(rlogz); free(rgap); free(rarg); free(clogz); free(cgap); free(carg); free(acc);
+                return 4;
             }
+        } else {
+            for (int t = 0; t < Gb; ++t)
+                if (!acc[t]) {
+                    A = t;
+                    break;
+                }
+            pos = A;
+        }
 
         /* Emit one target token. */
         int32_t y;
         double race_gap = INFINITY;
         if (lossy) {
             /* Reading: the lossy rules are greedy, so the target's own token
-             * is the centroid argmax at row A ([SD] "Greedy decoding"). */
-            y = carg[A];
+             * is the centroid argmax at row A ([SD] "Greedy decoding"); on a
+             * tree, at the last node of the kept path. */
+            y = carg[pos];
         } else {
             /* [PB] Sec. 5: residual normalize((p_A - q_A)+) after a rejection,
              * the bonus p_gamma when every draft survived; a zero residual
@@ -581,6 +660,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         }
 
         if (R->accept_len) R->accept_len[n] = A;
+        if (R->accept_pos) R->accept_pos[n] = pos;
         if (R->out_token) R->out_token[n] = y;
         if (R->race_gap) R->race_gap[n] = race_gap;
         for (int t = 0; t < T1; ++t) {
