@@ -9,7 +9,8 @@ the scan and the emitted token.  Prints one JSON line on stdout.
 
 The default workload is the Llama-3-8B-shaped head (B = 1, gamma = 7,
 d = 4096, |V| = 128256, K = 5, p_drop = 0.2, JS + majority).  --config picks
-another of the five workloads for inspection.
+another workload for inspection (0-4: chains; 5: naive matching on a 60-node
+token tree at the 70B head).
 """
 from __future__ import annotations
 
@@ -116,7 +117,7 @@ def cpu_baseline(w, seed, budget_s):
     while elapsed < budget_s:
         t0 = time.perf_counter()
         oracle.run(w.W, w.h, w.draft, w.q_hat, w.modes, w.K, w.p_drop, seed, seqs=np.array([calls % B], np.int32),
-                   n_threads=threads)
+                   n_threads=threads, tree_parent=w.tree_parent)
         elapsed += time.perf_counter() - t0
         done_pos += w.cfg.gamma + 1
         calls += 1
@@ -196,6 +197,7 @@ def main():
     W, h = dev_t(w.W), dev_t(w.h)
     draft = dev_t(w.draft.astype(np.int32))
     q_hat = dev_t(w.q_hat)
+    tree = dev_t(w.tree_parent) if w.tree_parent is not None else None
     dtype_code = Bd.DM_DTYPE_BF16 if cfg.dtype == wl.DTYPE_BF16 else Bd.DM_DTYPE_F32
     ver = Bd.Verifier(d=cfg.d, vocab=cfg.V, max_batch=cfg.B, gamma=cfg.gamma, k_max=cfg.K, dtype=dtype_code)
     seed = wl.perf_seed(cfg.index)
@@ -207,12 +209,14 @@ def main():
     else:
         W_run = W
     outs = {"accept_len": torch.empty(cfg.B, dtype=torch.int32, device=dev),
-            "out_token": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
+            "out_token": torch.empty(cfg.B, dtype=torch.int32, device=dev),
+            "accept_pos": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream(dev)
 
     def step():
         ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=stream.cuda_stream, outputs=outs,
-                w_layout=w_layout, temperature=args.temperature, top_k=args.top_k, top_p=args.top_p)
+                w_layout=w_layout, temperature=args.temperature, top_k=args.top_k, top_p=args.top_p,
+                tree_parent=tree)
 
     for _ in range(args.warmup):
         step()
@@ -266,7 +270,8 @@ def main():
         log(f"[bench] oracle {cpu['value']:.3f} positions/s on {cpu['cores']} threads")
 
     modes_desc = {"js": "JS+majority", "naive": "naive", "lossless": "lossless",
-                  "half_lossless_naive": "half lossless / half naive"}[cfg.modes]
+                  "half_lossless_naive": "half lossless / half naive",
+                  "tree": f"naive matching on a {cfg.gamma}-node, {cfg.tree_depth}-level token tree"}[cfg.modes]
     line = {
         "metric": "verified positions/sec (K=5 dropout heads + accept) and % HBM/MFMA roofline",
         "value": round(value, 1),

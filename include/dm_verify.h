@@ -14,7 +14,8 @@
  * rule", "Greedy decoding"; "Why speculative decoding preserves distributions
  * but may not be faster", Sec. 2 and the verify-round pseudocode of Sec. 5):
  *
- *   Lossy sequences (DM_MODE_NAIVE, DM_MODE_JS_MAJORITY), each position t:
+ *   Lossy sequences (DM_MODE_NAIVE, DM_MODE_JS_MAJORITY, DM_MODE_TREE_NAIVE),
+ *   each position t:
  *     keep[i, j] = Philox word (j/4, b*(gamma+1)+t, i, 0)[j%4] >= T,
  *                  T = min(floor(p_drop * 2^32 + 1/2), 2^32 - 1)  (Eq. (1))
  *     l^(i)[v]  = s * sum_j W[v, j] * h[b, t, j] * keep[i, j],
@@ -27,6 +28,20 @@
  *            (Eq. (7)), else reject                         (Algorithm 1)
  *   Emitted token: argmax of p-bar at the first rejected position A
  *            (A = gamma when all drafts pass).
+ *
+ *   Token trees (DM_MODE_TREE_NAIVE; "Speculative Decoding: Draft, Then
+ *     Verify", "Variants": one target pass verifies a tree of candidate
+ *     continuations under a tree-shaped attention mask; DropMatch Sec. 4.4:
+ *     on EAGLE3's trees the naive rule is the one applied).  Draft t is node
+ *     t+1 of the tree and hangs below position tree_parent[b, t] in [0, t]
+ *     (0 = the root); h[b, t+1] is the target's state after the path from
+ *     the root to that node, so a chain is tree_parent[b, t] = t.  Every
+ *     position runs the K dropout heads as above.  Draft t passes iff it is
+ *     one of the y^(i) at its parent position (Eq. (4)); a node is on a kept
+ *     path iff it and every node above it pass.  The round keeps the deepest
+ *     such path (on equal depths the node with the smallest index): A is its
+ *     depth, the emitted token the argmax of p-bar at its last node.  A
+ *     parent outside [0, t] rejects the draft and so every node below it.
  *
  *   Lossless sequences (DM_MODE_LOSSLESS): one undropped row per position,
  *     p_t = softmax(W h[b, t]).  With u_t = (Philox word (0, b*(gamma+1)+t,
@@ -82,7 +97,8 @@ typedef enum dm_w_layout {
 typedef enum dm_mode {
     DM_MODE_LOSSLESS = 0,    /* classical min(1, p/q) test, (p - q)+ residual */
     DM_MODE_NAIVE = 1,       /* DropMatch naive token matching, Eq. (4) */
-    DM_MODE_JS_MAJORITY = 2  /* DropMatch Algorithm 1, Eq. (6) then Eq. (7) */
+    DM_MODE_JS_MAJORITY = 2, /* DropMatch Algorithm 1, Eq. (6) then Eq. (7) */
+    DM_MODE_TREE_NAIVE = 3   /* Eq. (4) on a token tree (tree_parent below) */
 } dm_mode;
 
 /* Problem limits fixed at handle creation. */
@@ -90,7 +106,7 @@ typedef struct dm_verify_desc {
     int32_t d;         /* hidden size; multiple of 64, 64..65536 */
     int32_t vocab;     /* |V|, 1..524288 */
     int32_t max_batch; /* largest B a run may pass, 1..256 */
-    int32_t gamma;     /* drafted tokens per sequence, 0..31 (gamma+1 positions) */
+    int32_t gamma;     /* drafted tokens (tree nodes) per sequence, 0..63 (gamma+1 positions) */
     int32_t k_max;     /* largest K a run may pass, 1..16 */
     int32_t dtype;     /* dm_dtype of W and h */
 } dm_verify_desc;
@@ -134,8 +150,15 @@ typedef struct dm_verify_args {
     const int32_t* seq_gamma;  /* 0 <= seq_gamma[b] <= gamma */
     const int32_t* seq_heads;  /* 1 <= seq_heads[b] <= K */
     const float* seq_p_drop;   /* 0 <= seq_p_drop[b] < 1 */
-    int32_t* accept_len;    /* device out [B]: A, drafts accepted before the first rejection */
+    /* Token trees: device [B, gamma], the parent position of every draft of
+     * the TREE_NAIVE sequences (rows of other sequences are not read).
+     * Required iff a sequence is TREE_NAIVE and gamma > 0; with seq_gamma,
+     * only the first seq_gamma[b] entries of row b are read. */
+    const int32_t* tree_parent;
+    int32_t* accept_len;    /* device out [B]: A, drafts accepted (on a tree: depth of the kept path) */
     int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
+    int32_t* accept_pos;    /* device out [B] or NULL: position of the last kept node, whose p-bar
+                               (or p) gave out_token; A for chains */
     /* Optional device outputs for inspection; NULL = not written. */
     uint8_t* accept_flags;     /* [B, gamma] decision at every drafted position */
     int32_t* head_argmax;      /* [B, gamma+1, K]; -1 in heads 1.. of lossless sequences */

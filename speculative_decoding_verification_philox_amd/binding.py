@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libdmverify.so")
 
 DM_OK, DM_ERR_INVALID_ARGUMENT, DM_ERR_UNSUPPORTED, DM_ERR_HIP, DM_ERR_OUT_OF_MEMORY = 0, 1, 2, 3, 4
 DM_DTYPE_F32, DM_DTYPE_BF16 = 0, 1
-DM_MODE_LOSSLESS, DM_MODE_NAIVE, DM_MODE_JS_MAJORITY = 0, 1, 2
+DM_MODE_LOSSLESS, DM_MODE_NAIVE, DM_MODE_JS_MAJORITY, DM_MODE_TREE_NAIVE = 0, 1, 2, 3
 DM_W_ROW_MAJOR, DM_W_PANELS = 0, 1
 
 
@@ -42,8 +42,8 @@ class dm_verify_args(ctypes.Structure):
         ("w_layout", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("temperature", ctypes.c_float),
         ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("reserved", ctypes.c_uint32),
         ("seq_gamma", ctypes.c_void_p), ("seq_heads", ctypes.c_void_p), ("seq_p_drop", ctypes.c_void_p),
-        ("accept_len", ctypes.c_void_p),
-        ("out_token", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
+        ("tree_parent", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("out_token", ctypes.c_void_p),
+        ("accept_pos", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
         ("centroid_argmax", ctypes.c_void_p), ("head_logz", ctypes.c_void_p), ("centroid_logz", ctypes.c_void_p),
         ("js_heads", ctypes.c_void_p), ("js_draft", ctypes.c_void_p), ("logits", ctypes.c_void_p),
         ("mask_bits", ctypes.c_void_p), ("filter_count", ctypes.c_void_p), ("filter_logz", ctypes.c_void_p),
@@ -193,7 +193,8 @@ class Verifier:
         return t.data_ptr()
 
     def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, w_layout=DM_W_ROW_MAJOR,
-                  temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None, seq_p_drop=None, **debug):
+                  temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None, seq_p_drop=None,
+                  tree_parent=None, accept_pos=None, **debug):
         import torch
 
         D = self.desc
@@ -234,8 +235,12 @@ class Verifier:
                     raise ValueError(f"{name} must have one entry per sequence")
                 setattr(a, name, host.ctypes.data)
                 keep.append(host)
+        if tree_parent is not None and G > 0:
+            a.tree_parent = self._expect("tree_parent", tree_parent, (B, G), torch.int32, dev)
         a.accept_len = self._expect("accept_len", accept_len, (B,), torch.int32, dev)
         a.out_token = self._expect("out_token", out_token, (B,), torch.int32, dev)
+        if accept_pos is not None:
+            a.accept_pos = self._expect("accept_pos", accept_pos, (B,), torch.int32, dev)
         shapes = {"accept_flags": ((B, G), torch.uint8), "head_argmax": ((B, T1, K), torch.int32),
                   "centroid_argmax": ((B, T1), torch.int32), "head_logz": ((B, T1, K), torch.float32),
                   "centroid_logz": ((B, T1), torch.float32), "js_heads": ((B, G, K), torch.float32),
@@ -253,16 +258,18 @@ class Verifier:
 
     def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None,
             w_layout=DM_W_ROW_MAJOR, temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None,
-            seq_p_drop=None):
+            seq_p_drop=None, tree_parent=None):
         """Enqueue one verify step on `stream` (default: torch's current stream).
 
         W is row-major [vocab, d] (w_layout=DM_W_ROW_MAJOR) or the uint8
         buffer pack_w returns (w_layout=DM_W_PANELS).  temperature divides
         every logit row; top_k / top_p (0 / 1 = off) process the lossless
         target.  seq_gamma / seq_heads / seq_p_drop (host arrays of B, or
-        None) make the batch ragged.  Returns a dict with accept_len and
-        out_token (and every debug output when debug=True).  Preallocated
-        outputs can be passed in `outputs`."""
+        None) make the batch ragged.  tree_parent (device int32 [B, gamma])
+        gives the parent position of every draft of the TREE_NAIVE
+        sequences.  Returns a dict with accept_len, accept_pos and out_token
+        (and every debug output when debug=True).  Preallocated outputs can
+        be passed in `outputs`."""
         import torch
 
         D = self.desc
@@ -272,6 +279,7 @@ class Verifier:
         out = dict(outputs or {})
         out.setdefault("accept_len", torch.empty(B, dtype=torch.int32, device=dev))
         out.setdefault("out_token", torch.empty(B, dtype=torch.int32, device=dev))
+        out.setdefault("accept_pos", torch.empty(B, dtype=torch.int32, device=dev))
         if debug:
             out.setdefault("accept_flags", torch.zeros((B, G), dtype=torch.uint8, device=dev))
             out.setdefault("head_argmax", torch.empty((B, T1, K), dtype=torch.int32, device=dev))
@@ -288,7 +296,8 @@ class Verifier:
         dbg = {k: v for k, v in out.items() if k in DEBUG_OUTPUTS}
         args = self.make_args(W, h, draft, q_hat, modes, K, p_drop, seed, out["accept_len"], out["out_token"],
                               w_layout=w_layout, temperature=temperature, top_k=top_k, top_p=top_p,
-                              seq_gamma=seq_gamma, seq_heads=seq_heads, seq_p_drop=seq_p_drop, **dbg)
+                              seq_gamma=seq_gamma, seq_heads=seq_heads, seq_p_drop=seq_p_drop,
+                              tree_parent=tree_parent, accept_pos=out["accept_pos"], **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         dm_verify_run(self.handle, args, stream)

@@ -10,10 +10,11 @@ namespace dmv {
 
 constexpr int kMaxBatch = 256;
 constexpr int kMaxK = 16;
+constexpr int kMaxGamma = 63;  // drafts (tree nodes) per sequence: positions fit one wave
 constexpr int kMaskWords = kMaxBatch / 32;
 constexpr int kMaxDropValues = 8;  // distinct per-sequence dropout probabilities in one call
 
-enum Mode : int { kLossless = 0, kNaive = 1, kJs = 2 };
+enum Mode : int { kLossless = 0, kNaive = 1, kJs = 2, kTreeNaive = 3 };
 
 // Row layout of the LM-head GEMM ("slot layout").
 //
@@ -40,6 +41,7 @@ struct Plan {
     // sequences
     uint32_t lossless_bits[kMaskWords];
     uint32_t js_bits[kMaskWords];
+    uint32_t tree_bits[kMaskWords];  // naive matching on a token tree
     int n_lossy_seq, n_lossless_seq, n_js_seq;
     // sampling settings: row scales include 1 / temperature; the filter
     // (top-k, top-p) applies to lossless rows when `filter` is set

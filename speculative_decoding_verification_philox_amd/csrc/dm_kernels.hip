@@ -1079,6 +1079,40 @@ __device__ __forceinline__ int first_reject(bool reject, int G) {
     return rej ? __ffsll((long long)rej) - 1 : G;
 }
 
+// The round on a token tree ("Speculative Decoding: Draft, Then Verify",
+// "Variants"; DropMatch Sec. 4.4), one wave, lane t = draft t = node t+1:
+// `pass` is the rule's decision for the draft at its parent, `up` the
+// parent position (valid iff 0 <= up <= t).  A node is on a kept path iff
+// it and every node above it passed; the deepest such node wins, the
+// smallest index on equal depths.  Pointer jumping: each lane folds in the
+// pass flag and length of the segment above it, doubling the segment every
+// step, so six steps cover any path of up to 64 nodes.  Returns the depth
+// and writes the winner's position (0 = the root) to *pos.
+__device__ __forceinline__ int tree_walk(bool live, bool pass, int up, int lane, int* pos) {
+    const bool up_ok = live && up >= 0 && up <= lane;
+    int anc = up_ok ? up - 1 : -1;  // draft index of the parent node, -1 = the root
+    int ok = (up_ok && pass) ? 1 : 0;
+    int depth = 1;
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        const int src = anc < 0 ? lane : anc;
+        const int ok_a = __shfl(ok, src, 64);
+        const int depth_a = __shfl(depth, src, 64);
+        const int anc_a = __shfl(anc, src, 64);
+        if (anc >= 0) {
+            ok &= ok_a;
+            depth += depth_a;
+            anc = anc_a;
+        }
+    }
+    // deepest first, then the smallest lane: one max over (depth, 63 - lane)
+    int key = ok ? (depth << 6) | (63 - lane) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off, 64));
+    *pos = key ? 64 - (key & 63) : 0;
+    return key >> 6;
+}
+
 // JS partial sums of one (position, chunk): kJsPerThread consecutive entries
 // per thread, every load issued before any arithmetic (float4 loads when
 // rows are 16-byte aligned).  KMAX bounds K so the registers stay small.
@@ -1275,6 +1309,7 @@ constexpr int kFinishLoads = 16;  // JS chunk partials in flight per lane
 
 __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const int32_t* __restrict__ draft,
                                                            const float* __restrict__ q_hat,
+                                                           const int32_t* __restrict__ tree_parent,
                                                            const float* __restrict__ logits,
                                                            const RowStat* __restrict__ rowstat,
                                                            const RowStat* __restrict__ centstat,
@@ -1283,30 +1318,36 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                                                            const FiltStat* __restrict__ filt,
                                                            int32_t* __restrict__ accept_len,
                                                            int32_t* __restrict__ out_token,
+                                                           int32_t* __restrict__ accept_pos,
                                                            uint8_t* __restrict__ dbg_flags,
                                                            float* __restrict__ dbg_js_heads,
                                                            float* __restrict__ dbg_js_draft) {
-    __shared__ float s_js[32][kMaxK + 1];
+    __shared__ float s_js[kMaxGamma + 1][kMaxK + 1];
     const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = P.K, G = P.G, T1 = P.T1;  // layout strides
     const int Gb = seq_G(P, b), Kb = seq_K(P, b);  // this sequence's drafts and heads
     const bool lossless = bit_of(P.lossless_bits, b);
     const bool js = bit_of(P.js_bits, b);
+    const bool tree = bit_of(P.tree_bits, b);
 
-    // wave 0, lane t: the inputs of the decision at position t
-    int x = -1, cent_idx = 0;
+    // wave 0, lane t: the inputs of the decision for draft t, made by the
+    // heads at position t (a chain) or at the draft's parent (a tree)
+    int x = -1, cent_idx = 0, up = -1;
     int head_idx[kMaxK];
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) head_idx[i] = -1;
     unsigned long long best_r = 0ull, best_p = 0ull;
     if (wave == 0) {
         if (lane < Gb) x = draft[b * G + lane];
+        if (tree && lane < Gb) up = tree_parent[b * G + lane];
         if (!lossless) {
             if (lane <= Gb) cent_idx = centstat[b * T1 + lane].idx;
+            // a parent outside [0, t] rejects the draft; read position t instead
+            const int at = (tree && up >= 0 && up <= lane) ? up : lane;
             if (lane < Gb) {
 #pragma unroll
                 for (int i = 0; i < kMaxK; ++i)
-                    if (i < Kb) head_idx[i] = rowstat[(b * T1 + lane) * K + i].idx;
+                    if (i < Kb) head_idx[i] = rowstat[(b * T1 + at) * K + i].idx;
             }
         } else if (lane == 0) {
             best_r = race_best[2 * b];
@@ -1362,14 +1403,22 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                     for (int i = 0; i < Kb; ++i) dbg_js_heads[(size_t)(b * G + lane) * K + i] = s_js[lane][i];
             } else {
                 accept = valid && count > 0;  // DropMatch Eq. (4)
+                if (tree && !(up >= 0 && up <= lane)) accept = false;
             }
         }
         if (dbg_flags) dbg_flags[b * G + lane] = accept ? 1 : 0;
     }
-    const int A = first_reject(lane < Gb && !accept, Gb);
-    const int token_lossy = __shfl(cent_idx, A, 64);  // greedy on the centroid at A
+    int A, pos;
+    if (tree) {
+        A = tree_walk(lane < Gb, accept, up, lane, &pos);
+    } else {
+        A = first_reject(lane < Gb && !accept, Gb);
+        pos = A;
+    }
+    const int token_lossy = __shfl(cent_idx, pos, 64);  // greedy on the centroid at the last kept node
     if (lane == 0) {
         accept_len[b] = A;
+        if (accept_pos) accept_pos[b] = pos;
         if (lossless) {
             const unsigned long long best = best_r ? best_r : best_p;
             out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
@@ -1841,18 +1890,20 @@ hipError_t launch_filter(const Plan& P, const float* logits, const RowStat* rows
     return hipGetLastError();
 }
 
-hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const float* logits,
-                        const RowStat* rowstat, const RowStat* centstat, float* jspart,
+hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const int32_t* tree_parent,
+                        const float* logits, const RowStat* rowstat, const RowStat* centstat, float* jspart,
                         unsigned long long* race_best, const FiltStat* filt, int32_t* accept_len, int32_t* out_token,
-                        uint8_t* dbg_flags, float* dbg_js_heads, float* dbg_js_draft, hipStream_t st) {
+                        int32_t* accept_pos, uint8_t* dbg_flags, float* dbg_js_heads, float* dbg_js_draft,
+                        hipStream_t st) {
     if (P.blk_js + P.blk_race > 0) {
         hipLaunchKernelGGL(k_vocab, dim3(P.blk_js + P.blk_race), dim3(kVocabThreads), 0, st, P, draft, q_hat, logits,
                            rowstat, centstat, jspart, race_best, filt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishThreads), 0, st, P, draft, q_hat, logits, rowstat, centstat,
-                       jspart, race_best, filt, accept_len, out_token, dbg_flags, dbg_js_heads, dbg_js_draft);
+    hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishThreads), 0, st, P, draft, q_hat, tree_parent, logits,
+                       rowstat, centstat, jspart, race_best, filt, accept_len, out_token, accept_pos, dbg_flags,
+                       dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ int check_desc(const dm_verify_desc* D) {
     if (!D) return DM_ERR_INVALID_ARGUMENT;
     if (D->d <= 0 || D->vocab <= 0 || D->max_batch <= 0 || D->gamma < 0 || D->k_max <= 0)
         return DM_ERR_INVALID_ARGUMENT;
-    if (D->max_batch > kMaxBatch || D->gamma > 31 || D->k_max > kMaxK || D->vocab > kMaxVocab)
+    if (D->max_batch > kMaxBatch || D->gamma > kMaxGamma || D->k_max > kMaxK || D->vocab > kMaxVocab)
         return DM_ERR_INVALID_ARGUMENT;
     if (D->dtype != DM_DTYPE_F32 && D->dtype != DM_DTYPE_BF16) return DM_ERR_UNSUPPORTED;
     if (D->d % 64 != 0 || D->d > 65536) return DM_ERR_UNSUPPORTED;
@@ -66,11 +66,12 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
         return DM_ERR_INVALID_ARGUMENT;
     if (!a->W || !a->h || !a->modes || !a->accept_len || !a->out_token) return DM_ERR_INVALID_ARGUMENT;
     if (D->gamma > 0 && !a->draft) return DM_ERR_INVALID_ARGUMENT;
-    bool need_q = false;
+    bool need_q = false, need_tree = false;
     for (int b = 0; b < a->batch; ++b) {
         uint8_t m = a->modes[b];
-        if (m > DM_MODE_JS_MAJORITY) return DM_ERR_INVALID_ARGUMENT;
-        if (m != DM_MODE_NAIVE) need_q = true;
+        if (m > DM_MODE_TREE_NAIVE) return DM_ERR_INVALID_ARGUMENT;
+        if (m == DM_MODE_LOSSLESS || m == DM_MODE_JS_MAJORITY) need_q = true;
+        if (m == DM_MODE_TREE_NAIVE) need_tree = true;
         if (a->seq_gamma && (a->seq_gamma[b] < 0 || a->seq_gamma[b] > D->gamma)) return DM_ERR_INVALID_ARGUMENT;
         if (a->seq_heads && (a->seq_heads[b] < 1 || a->seq_heads[b] > a->K)) return DM_ERR_INVALID_ARGUMENT;
         if (a->seq_p_drop && !(a->seq_p_drop[b] >= 0.0f && a->seq_p_drop[b] < 1.0f)) return DM_ERR_INVALID_ARGUMENT;
@@ -88,10 +89,11 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
         }
     }
     if (need_q && D->gamma > 0 && !a->q_hat) return DM_ERR_INVALID_ARGUMENT;
+    if (need_tree && D->gamma > 0 && !a->tree_parent) return DM_ERR_INVALID_ARGUMENT;
     if (!aligned(a->W, 16) || !aligned(a->h, 16)) return DM_ERR_UNSUPPORTED;
     const void* four[] = {a->draft, a->q_hat, a->accept_len, a->out_token, a->head_argmax, a->centroid_argmax,
                           a->head_logz, a->centroid_logz, a->js_heads, a->js_draft, a->logits, a->mask_bits,
-                          a->filter_count, a->filter_logz};
+                          a->filter_count, a->filter_logz, a->tree_parent, a->accept_pos};
     for (const void* p : four)
         if (p && !aligned(p, 4)) return DM_ERR_UNSUPPORTED;
     return DM_OK;
@@ -376,6 +378,7 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     for (int b = 0; b < a->batch; ++b) {
         if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
+        if (a->modes[b] == DM_MODE_TREE_NAIVE) P.tree_bits[b >> 5] |= 1u << (b & 31);
     }
     // temperature divides every row: folded into the row scales
     const double temp = a->temperature > 0.0f ? (double)a->temperature : 1.0;
@@ -441,8 +444,9 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, a->head_argmax, a->head_logz, a->centroid_argmax,
                           a->centroid_logz, st));
     DM_TRY(launch_filter(P, logits, h->rowstat, h->filt, a->filter_count, a->filter_logz, st));
-    DM_TRY(launch_vocab(P, a->draft, a->q_hat, logits, h->rowstat, h->centstat, h->jspart, h->race, h->filt,
-                        a->accept_len, a->out_token, a->accept_flags, a->js_heads, a->js_draft, st));
+    DM_TRY(launch_vocab(P, a->draft, a->q_hat, a->tree_parent, logits, h->rowstat, h->centstat, h->jspart, h->race,
+                        h->filt, a->accept_len, a->out_token, a->accept_pos, a->accept_flags, a->js_heads,
+                        a->js_draft, st));
 #undef DM_TRY
     return DM_OK;
 }

@@ -18,6 +18,16 @@ Recipe (shapes from the DropMatch paper's Llama-3 / Qwen3 settings, Sec. 4):
     normalised in fp64 and stored fp32 (T_q = 1, sigma = 2; config 4:
     T_q = 0.8, sigma = 1.5).
   * draft_t = t* with probability 0.7, else a draw from q_hat_t.
+
+Token trees (tree_depth > 0; a stand-in for EAGLE3's draft trees, whose
+sizes the pages do not give): the gamma nodes are split over tree_depth
+levels as evenly as possible, in level order.  A node of level l > 1 hangs
+below a node of level l - 1 drawn with weight 1 / (rank + 1) (earlier, more
+probable candidates gather more children, as a reranked top-k tree does);
+level 1 hangs below the root; within a level the nodes are sorted by parent.
+Draft t's q_hat row is built from the logits at its parent position; the
+first child of a parent is t*(parent) with probability 0.7, else a draw from
+q_hat, and later children are draws from q_hat distinct from their siblings.
 """
 from __future__ import annotations
 
@@ -27,8 +37,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-LOSSLESS, NAIVE, JS = 0, 1, 2
-MODE_NAMES = {LOSSLESS: "lossless", NAIVE: "naive", JS: "js_majority"}
+LOSSLESS, NAIVE, JS, TREE_NAIVE = 0, 1, 2, 3
+MODE_NAMES = {LOSSLESS: "lossless", NAIVE: "naive", JS: "js_majority", TREE_NAIVE: "tree_naive"}
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
@@ -44,10 +54,11 @@ class Config:
     p_drop: float
     dtype: int
     planted: float
-    modes: str  # "js", "naive", "lossless", or "half_lossless_naive"
+    modes: str  # "js", "naive", "lossless", "half_lossless_naive" or "tree"
     q_temp: float = 1.0
     q_sigma: float = 2.0
     index: int = 0
+    tree_depth: int = 0  # > 0: the drafts form a token tree of this many levels
 
     @property
     def positions(self) -> int:
@@ -66,6 +77,10 @@ CONFIGS = [
            planted=0.8, modes="js", index=3),
     Config("wide_mixed", B=64, gamma=5, d=5120, V=151936, K=8, p_drop=0.2, dtype=DTYPE_BF16,
            planted=0.9, modes="half_lossless_naive", q_temp=0.8, q_sigma=1.5, index=4),
+    # naive matching on a draft tree at the 70B head (DropMatch Sec. 4.4, Table 7: K = 5, p_drop = 0.3,
+    # draft length up to 10): 60 nodes over 10 levels
+    Config("eagle3_70b_tree", B=1, gamma=60, d=8192, V=128256, K=5, p_drop=0.3, dtype=DTYPE_BF16,
+           planted=0.9, modes="tree", tree_depth=10, index=5),
 ]
 
 
@@ -79,6 +94,7 @@ class Workload:
     modes: np.ndarray   # uint8 [B]
     t_star: np.ndarray  # int32 [B, gamma+1] planted / reference tokens
     planted: np.ndarray  # bool [B, gamma+1]
+    tree_parent: np.ndarray | None = None  # int32 [B, gamma] parent position of every draft (trees)
 
     @property
     def K(self):
@@ -153,11 +169,28 @@ def modes_for(cfg: Config, B: int | None = None) -> np.ndarray:
         return np.full(B, NAIVE, np.uint8)
     if cfg.modes == "lossless":
         return np.full(B, LOSSLESS, np.uint8)
+    if cfg.modes == "tree":
+        return np.full(B, TREE_NAIVE, np.uint8)
     if cfg.modes == "half_lossless_naive":
         m = np.full(B, NAIVE, np.uint8)
         m[: B // 2] = LOSSLESS
         return m
     raise ValueError(cfg.modes)
+
+
+def tree_parents(rng: np.random.Generator, G: int, depth: int) -> np.ndarray:
+    """Parent position of each of G drafts for a tree of `depth` levels
+    (the recipe in the module docstring)."""
+    depth = max(1, min(depth, G))
+    sizes = [G // depth + (1 if l < G % depth else 0) for l in range(depth)] if G else []
+    parents, prev, node = [], [0], 1
+    for n in sizes:
+        w = 1.0 / np.arange(1, len(prev) + 1)
+        ups = np.sort(rng.choice(np.asarray(prev), size=n, p=w / w.sum()))
+        parents.extend(int(u) for u in ups)
+        prev = list(range(node, node + n))
+        node += n
+    return np.asarray(parents, np.int32)
 
 
 def generate(cfg: Config | int, seed_base: int = 1000, **overrides) -> Workload:
@@ -168,6 +201,7 @@ def generate(cfg: Config | int, seed_base: int = 1000, **overrides) -> Workload:
         cfg = dataclasses.replace(cfg, **overrides)
     root = np.random.SeedSequence(seed_base + cfg.index)
     s_w, s_h, s_q, s_draft = root.spawn(4)
+    (s_tree,) = root.spawn(1)
     B, T1, d, V, G = cfg.B, cfg.gamma + 1, cfg.d, cfg.V, cfg.gamma
 
     W = _draw_w(s_w, V, d, cfg.dtype)
@@ -182,9 +216,16 @@ def generate(cfg: Config | int, seed_base: int = 1000, **overrides) -> Workload:
     hf = hf.astype(np.float32).reshape(B, T1, d)
     h = to_bf16_bits(hf) if cfg.dtype == DTYPE_BF16 else hf
 
-    # Draft distributions around the target's own logits (drafted positions only).
+    # Draft distributions around the target's own logits (drafted positions
+    # only; a tree's draft t at its parent position).
+    parents = None
+    if cfg.tree_depth > 0:
+        gt = np.random.Generator(np.random.PCG64(s_tree))
+        parents = np.stack([tree_parents(gt, G, cfg.tree_depth) for _ in range(B)]).reshape(B, G)
     H = as_f32(h)[:, :G, :].reshape(-1, d)
     logits = _target_logits(W, H) if G > 0 else np.zeros((0, V), np.float32)
+    if parents is not None:
+        logits = logits.reshape(B, G, V)[np.arange(B)[:, None], parents].reshape(B * G, V)
     gq = np.random.Generator(np.random.PCG64(s_q))
     q_hat = np.empty((B * G, V), dtype=np.float32)
     for r in range(B * G):
@@ -196,13 +237,30 @@ def generate(cfg: Config | int, seed_base: int = 1000, **overrides) -> Workload:
 
     gd = np.random.Generator(np.random.PCG64(s_draft))
     draft = np.empty((B, G), dtype=np.int32)
+
+    def from_q(b, t):
+        cdf = np.cumsum(q_hat[b, t].astype(np.float64))
+        return int(min(np.searchsorted(cdf, gd.random() * cdf[-1], side="right"), V - 1))
+
     for b in range(B):
+        if parents is None:
+            for t in range(G):
+                draft[b, t] = t_star[b, t] if gd.random() < 0.7 else from_q(b, t)
+            continue
+        used = {}
         for t in range(G):
-            if gd.random() < 0.7:
-                draft[b, t] = t_star[b, t]
+            up = int(parents[b, t])
+            sib = used.setdefault(up, set())
+            if not sib and gd.random() < 0.7:
+                x = int(t_star[b, up])
             else:
-                cdf = np.cumsum(q_hat[b, t].astype(np.float64))
-                draft[b, t] = int(min(np.searchsorted(cdf, gd.random() * cdf[-1], side="right"), V - 1))
+                x = from_q(b, t)
+                for _ in range(50):  # siblings are distinct candidates
+                    if x not in sib:
+                        break
+                    x = from_q(b, t)
+            sib.add(x)
+            draft[b, t] = x
 
     return Workload(cfg=cfg, W=W, h=h, draft=draft, q_hat=q_hat, modes=modes_for(cfg, B),
-                    t_star=t_star, planted=planted)
+                    t_star=t_star, planted=planted, tree_parent=parents)

@@ -13,7 +13,9 @@ Parity bar (from the verify step's contract):
     at A, the emitted token.
 An argmax (or emitted token) may differ only where the oracle's top-2 gap is
 below the same 1e-4 (the fp32 path cannot order closer values reliably);
-those are counted too.
+those are counted too.  On a token tree any decision can move the kept path,
+so a sequence with a near-tie decision anywhere is exempt from the result
+check (and counted).
 """
 from __future__ import annotations
 
@@ -96,12 +98,17 @@ def weights(ver, inp: Inputs, layout):
     return inp.W
 
 
-def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None, ragged=None):
-    """`ragged`: dict of seq_gamma / seq_heads / seq_p_drop host arrays."""
+def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None, ragged=None,
+            tree=None):
+    """`ragged`: dict of seq_gamma / seq_heads / seq_p_drop host arrays;
+    `tree`: int32 [B, gamma] parent positions (copied to the device)."""
     import torch
 
+    tp = None
+    if tree is not None and inp.h.shape[1] > 1:
+        tp = to_device(np.ascontiguousarray(tree, dtype=np.int32))
     out = ver.run(weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug,
-                  w_layout=layout, **(sampling or {}), **(ragged or {}))
+                  w_layout=layout, tree_parent=tp, **(sampling or {}), **(ragged or {}))
     torch.cuda.synchronize()
     res = {}
     for k, v in out.items():
@@ -210,23 +217,31 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False, rag
         # accepted length and emitted token
         A_o = int(ora["accept_len"][r])
         rep.sequences += 1
-        decisive = near[: min(A_o + 1, G)].any() if G > 0 else False
+        pos_o = int(ora["accept_pos"][r])
+        if mode == wl.TREE_NAIVE:
+            decisive = bool(near.any())
+        else:
+            decisive = near[: min(A_o + 1, G)].any() if G > 0 else False
         if mode == wl.LOSSLESS:
             tok_near = ora["race_gap"][r] < RACE_GAP or bool(fnear[A_o])
         else:
-            tok_near = ora["centroid_gap"][r][A_o] < MARGIN
+            tok_near = ora["centroid_gap"][r][pos_o] < MARGIN
         if decisive or tok_near:
             rep.sequence_exempt += 1
             continue
         assert int(gpu["accept_len"][b]) == A_o, f"accept_len of sequence {b}: gpu {gpu['accept_len'][b]} oracle {A_o}"
+        if "accept_pos" in gpu:
+            assert int(gpu["accept_pos"][b]) == pos_o, (
+                f"accept_pos of sequence {b}: gpu {gpu['accept_pos'][b]} oracle {pos_o}")
         assert int(gpu["out_token"][b]) == int(ora["out_token"][r]), (
             f"out_token of sequence {b}: gpu {gpu['out_token'][b]} oracle {ora['out_token'][r]}")
     return rep
 
 
-def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None, ragged=None):
+def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None, ragged=None,
+               tree=None):
     rg = dict(ragged or {})
     if "seq_heads" in rg:
         rg["seq_K"] = rg.pop("seq_heads")
     return oracle.run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=seqs, want_logits=debug,
-                      want_masks=debug and W.shape[1] % 32 == 0, **(sampling or {}), **rg)
+                      want_masks=debug and W.shape[1] % 32 == 0, tree_parent=tree, **(sampling or {}), **rg)

@@ -19,9 +19,9 @@ hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*
 hipError_t launch_filter(const Plan&, const float*, const RowStat*, FiltStat*, int32_t*, float*, hipStream_t) {
     return hipSuccess;
 }
-hipError_t launch_vocab(const Plan&, const int32_t*, const float*, const float*, const RowStat*, const RowStat*,
-                        float*, unsigned long long*, const FiltStat*, int32_t*, int32_t*, uint8_t*, float*, float*,
-                        hipStream_t) {
+hipError_t launch_vocab(const Plan&, const int32_t*, const float*, const int32_t*, const float*, const RowStat*,
+                        const RowStat*, float*, unsigned long long*, const FiltStat*, int32_t*, int32_t*, int32_t*,
+                        uint8_t*, float*, float*, hipStream_t) {
     return hipSuccess;
 }
 hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipSuccess; }
@@ -44,7 +44,7 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     int nl = 0, nj = 0;
     for (int b = 0; b < B; ++b) {
         s = s * 1103515245u + 12345u;
-        modes[b] = (uint8_t)((s >> 16) % 3);
+        modes[b] = (uint8_t)((s >> 16) % 4);
         if (seed == 0) modes[b] = DM_MODE_JS_MAJORITY;
         if (seed == 1) modes[b] = DM_MODE_LOSSLESS;
         nl += modes[b] == DM_MODE_LOSSLESS;
@@ -55,6 +55,7 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     for (int b = 0; b < B; ++b) {
         if (modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
+        if (modes[b] == DM_MODE_TREE_NAIVE) P.tree_bits[b >> 5] |= 1u << (b & 31);
     }
     Sizes sz = workspace_sizes(D);
     const int T1 = gamma + 1;
@@ -75,7 +76,7 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     CHECK(nl == 0 || ((long long)P.race_chunks * P.race_chunk >= V && (long long)(P.race_chunks - 1) * P.race_chunk < V),
           "race chunks\n");
     CHECK(P.blk_js == P.n_js_pos * P.js_chunks && P.blk_race == nl * P.race_chunks, "block count\n");
-    CHECK(gamma <= 32, "gamma beyond the finishing kernel's JS table\n");
+    CHECK(gamma <= kMaxGamma && T1 <= 64, "gamma beyond one wave of positions\n");
     std::vector<int> seen((size_t)B * T1 * K, 0);
     for (int rho = 0; rho < P.R_phys; ++rho) {
         RowInfo ri = row_info(P, rho);
@@ -157,7 +158,7 @@ int main() {
         for (int K : Ks) {
             if (K > kmax) continue;
             for (int B : {1, 2, 7, 32, 64, 200, 256})
-                for (int gamma : {0, 4, 7, 31})
+                for (int gamma : {0, 4, 7, 31, 63})
                     for (unsigned seed : {0u, 1u, 2u, 3u}) {
                         for (int wp = 0; wp <= 1; ++wp) {
                             check_case(512, 5003, 256, gamma, kmax, B, K, seed, wp);

@@ -48,10 +48,11 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header(lib):
     # sizes follow from the field lists in include/dm_verify.h on LP64
     assert ctypes.sizeof(B.dm_verify_desc) == 24
-    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 3 * 8 + 2 * 8 + 11 * 8
+    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 4 * 8 + 3 * 8 + 11 * 8
     assert B.dm_verify_args.seed.offset == 56
     assert B.dm_verify_args.temperature.offset == 64 and B.dm_verify_args.seq_gamma.offset == 80
-    assert B.dm_verify_args.accept_len.offset == 104
+    assert B.dm_verify_args.tree_parent.offset == 104 and B.dm_verify_args.accept_len.offset == 112
+    assert B.dm_verify_args.accept_pos.offset == 128 and B.dm_verify_args.accept_flags.offset == 136
 
 
 def desc(**kw):
@@ -93,7 +94,7 @@ def test_valid_arguments_pass(lib):
     ("max_batch", 0, B.DM_ERR_INVALID_ARGUMENT),
     ("max_batch", 257, B.DM_ERR_INVALID_ARGUMENT),
     ("gamma", -1, B.DM_ERR_INVALID_ARGUMENT),
-    ("gamma", 32, B.DM_ERR_INVALID_ARGUMENT),
+    ("gamma", 64, B.DM_ERR_INVALID_ARGUMENT),
     ("k_max", 0, B.DM_ERR_INVALID_ARGUMENT),
     ("k_max", 17, B.DM_ERR_INVALID_ARGUMENT),
     ("dtype", 7, B.DM_ERR_UNSUPPORTED),
@@ -133,6 +134,8 @@ def test_bad_desc(lib, field, value, status):
     (dict(top_p=float("nan")), B.DM_ERR_INVALID_ARGUMENT),
     (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
     (dict(filter_count=0x10002), B.DM_ERR_UNSUPPORTED),
+    (dict(accept_pos=0x10002), B.DM_ERR_UNSUPPORTED),
+    (dict(modes=(3, 1), tree_parent=0x10002), B.DM_ERR_UNSUPPORTED),
     (dict(seq_gamma=[5, 0]), B.DM_ERR_INVALID_ARGUMENT),
     (dict(seq_gamma=[-1, 0]), B.DM_ERR_INVALID_ARGUMENT),
     (dict(seq_heads=[0, 5]), B.DM_ERR_INVALID_ARGUMENT),
@@ -165,7 +168,18 @@ def test_sampling_settings_in_range_pass(lib, change):
 
 
 def test_mode_out_of_range(lib):
-    assert B.dm_verify_check(desc(), args(modes=(2, 3))) == B.DM_ERR_INVALID_ARGUMENT
+    assert B.dm_verify_check(desc(), args(modes=(2, 4))) == B.DM_ERR_INVALID_ARGUMENT
+
+
+def test_tree_sequences_need_parents(lib):
+    fake = 0x10000
+    tree = B.DM_MODE_TREE_NAIVE
+    assert B.dm_verify_check(desc(), args(modes=(tree, 1), q_hat=None)) == B.DM_ERR_INVALID_ARGUMENT
+    assert B.dm_verify_check(desc(), args(modes=(tree, 1), q_hat=None, tree_parent=fake)) == B.DM_OK
+    assert B.dm_verify_check(desc(), args(modes=(tree, 0), tree_parent=fake, accept_pos=fake)) == B.DM_OK
+    assert B.dm_verify_check(desc(gamma=0), args(modes=(tree, tree), draft=None, q_hat=None)) == B.DM_OK
+    # chains ignore the parents; the largest tree fills one wave of positions
+    assert B.dm_verify_check(desc(gamma=63), args(modes=(1, 2), tree_parent=fake)) == B.DM_OK
 
 
 def test_naive_needs_no_draft_distribution(lib):

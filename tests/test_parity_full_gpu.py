@@ -1,4 +1,5 @@
-"""GPU parity at the five workloads' full sizes.
+"""GPU parity at the workloads' full sizes (the five chain workloads and the
+token tree at the 70B head).
 
 Each test runs the library on the same inputs with W in both orders
 (row-major and panels), each twice: once exactly as bench.py times it (no
@@ -31,12 +32,13 @@ def _full(cfg_index, seqs, p_values=None, seeds=(None,)):
         for seed in seeds:
             seed = wl.perf_seed(cfg.index) if seed is None else seed
             print(f"  p_drop={p} seed={seed:#x} oracle sequences={list(seqs)}", flush=True)
-            o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs)
+            o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs, tree=w.tree_parent)
             for layout in P.LAYOUTS:
-                g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=layout)
-                g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=layout)
-                np.testing.assert_array_equal(g_bench["accept_len"], g_dbg["accept_len"])
-                np.testing.assert_array_equal(g_bench["out_token"], g_dbg["out_token"])
+                g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=layout,
+                                    tree=w.tree_parent)
+                g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=layout, tree=w.tree_parent)
+                for k in ("accept_len", "accept_pos", "out_token"):
+                    np.testing.assert_array_equal(g_bench[k], g_dbg[k], err_msg=k)
                 rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
                 rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
     ver.close()
@@ -58,3 +60,8 @@ def test_config3_batched_70b_sampled():
 
 def test_config4_wide_mixed_sampled():
     _full(4, seqs=[0, 31, 32, 63])
+
+
+def test_config5_eagle3_70b_tree():
+    rep = _full(5, seqs=[0])
+    assert rep.sequences == 4

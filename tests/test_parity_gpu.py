@@ -21,17 +21,17 @@ def layout(request):
 
 
 def _check(W, h, draft, q, modes, K, p, seeds, max_batch=None, report=None, layout=P.ROW_MAJOR, sampling=None,
-           ragged=None):
+           ragged=None, tree=None):
     ver = P.make_verifier(W, h, K, max_batch)
     inp = P.Inputs(W, h, draft, q)
     rep = P.Report()
     smp = sampling or {}
     filtered = 0 < smp.get("top_k", 0) < W.shape[0] or 0 < smp.get("top_p", 0.0) < 1
     for seed in seeds:
-        print(f"  seed={seed} B={h.shape[0]} K={K} p={p} modes={np.bincount(modes, minlength=3)} layout={layout}"
-              f" sampling={smp}", flush=True)
-        g = P.run_gpu(ver, inp, modes, K, p, seed, layout=layout, sampling=sampling, ragged=ragged)
-        o = P.oracle_run(W, h, draft, q, modes, K, p, seed, sampling=sampling, ragged=ragged)
+        print(f"  seed={seed} B={h.shape[0]} gamma={h.shape[1] - 1} K={K} p={p} modes={np.bincount(modes, minlength=4)}"
+              f" layout={layout} sampling={smp} tree={tree is not None}", flush=True)
+        g = P.run_gpu(ver, inp, modes, K, p, seed, layout=layout, sampling=sampling, ragged=ragged, tree=tree)
+        o = P.oracle_run(W, h, draft, q, modes, K, p, seed, sampling=sampling, ragged=ragged, tree=tree)
         rep.add(P.compare(g, o, modes, K, filtered=filtered, ragged=ragged))
     ver.close()
     print(rep, flush=True)
