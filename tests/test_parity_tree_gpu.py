@@ -82,3 +82,14 @@ def test_chain_parents_give_the_naive_chain_bit_for_bit(layout):
             np.testing.assert_array_equal(a[k], b[k], err_msg=k)
         np.testing.assert_array_equal(b["accept_pos"], b["accept_len"])
     ver.close()
+
+
+def test_tree_with_temperature_and_no_accepted_node(layout):
+    """Temperature divides every head row of a tree too; a tree whose drafts
+    all fail emits the centroid argmax at the root."""
+    w = _tree(0, B=3, gamma=12, tree_depth=3, planted=0.9)
+    _check(w.W, w.h, w.draft, w.q_hat, w.modes, 5, 0.2, [1, 2], layout=layout, tree=w.tree_parent,
+           sampling=dict(temperature=0.7))
+    bad = np.full_like(w.draft, w.cfg.V + 5)  # out of range: every draft is rejected
+    g = _check(w.W, w.h, bad, w.q_hat, w.modes, 5, 0.2, [3], layout=layout, tree=w.tree_parent)
+    assert g.sequences == 3
