@@ -265,23 +265,46 @@ __device__ __forceinline__ int row16_min(int x) {
 }
 
 // (max, sum exp, lowest argmax) of the 64 values held as four per lane by
-// the 16 lanes of a row; columns >= V are left out.
+// the 16 lanes of a row; columns >= V are left out.  Selects instead of
+// branches: a left-out column adds exactly 0 to the sum and -inf to the max,
+// so the result is the same as skipping it.
 template <int G>
 __device__ __forceinline__ Stat row16_stat(const float (&x)[G], const bool (&ok)[G], int col0) {
     float m = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        if (ok[g]) m = fmaxf(m, x[g]);
+    for (int g = 0; g < G; ++g) m = fmaxf(m, ok[g] ? x[g] : -INFINITY);
     m = row16_max(m);
     float s = 0.0f;
     int idx = 0x7fffffff;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        if (ok[g]) {
-            s += __expf(x[g] - m);
-            if (x[g] == m) idx = min(idx, col0 + 16 * g);
-        }
+    for (int g = 0; g < G; ++g) {
+        const float e = __expf(x[g] - m);
+        s += ok[g] ? e : 0.0f;
+        idx = (ok[g] && x[g] == m) ? min(idx, col0 + 16 * g) : idx;
+    }
     return Stat{m, row16_sum(s), row16_min(idx)};
+}
+
+// Running centroid of the lossy positions in a lane group: slot lam of the
+// group is head i = lam mod K of position lam / K.  The head rows are summed
+// in head order as they go by (the order every kernel uses for the centroid,
+// see centroid_logit) and the position's statistics are taken at its last
+// head.  lam and K are uniform, so the branch is too.
+template <int G>
+__device__ __forceinline__ void centroid_slot(const Plan& P, int lam, const float (&x)[G], float (&csum)[G],
+                                              const bool (&ok)[G], int col0, int pos_base, bool write,
+                                              Stat* __restrict__ dst) {
+    const int slot = lam / P.K, i = lam - slot * P.K;
+#pragma unroll
+    for (int g = 0; g < G; ++g) csum[g] = i == 0 ? x[g] : csum[g] + x[g];
+    if (i == P.K - 1 && slot < P.ppg) {
+        const float inv = lossy_pos_inv_k(P, pos_base + slot);
+        float xc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) xc[g] = csum[g] * inv;
+        const Stat st = row16_stat<G>(xc, ok, col0);
+        if (write) dst[slot] = st;
+    }
 }
 
 template <bool BF16, int MSUB>
@@ -388,26 +411,14 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
     const int npt = P.GR * P.ppg;
     const bool lossy_tile = tile < P.tiles_lossy;
     if (lossy_tile) {
-        for (int slot = 0; slot < P.ppg; ++slot) {
-            const int first = slot * P.K;
-            const float inv = lossy_pos_inv_k(P, tile * npt + grp * P.ppg + slot);
+        float csum[G];
+#pragma unroll
+        for (int lam = 0; lam < 4 * MSUB; ++lam) {
             float x[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                // head rows first .. first + K - 1 of this lane group, summed in head order
-                float sum = 0.0f;
-#pragma unroll
-                for (int lam = 0; lam < 4 * MSUB; ++lam) {
-                    const int i = lam - first;
-                    if (i >= 0 && i < P.K) {
-                        const float v = acc[g][lam >> 2][lam & 3];
-                        sum = i == 0 ? v : sum + v;
-                    }
-                }
-                x[g] = sum * inv;
-            }
-            const Stat st = row16_stat<G>(x, ok, col0);
-            if (c == 0) s_st[wave][ROWS + grp * P.ppg + slot] = st;
+            for (int g = 0; g < G; ++g) x[g] = acc[g][lam >> 2][lam & 3];
+            centroid_slot<G>(P, lam, x, csum, ok, col0, tile * npt + grp * P.ppg, c == 0,
+                             &s_st[wave][ROWS + grp * P.ppg]);
         }
     }
     __syncthreads();
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
 #pragma unroll
         for (int g = 0; g < G; ++g) ok[g] = my_panel < P.n_panels && col0 + 16 * g < P.V;
 #pragma unroll
-        for (int m = 0; m < MSUB; ++m)
+        for (int m = 0; m < MSUB; ++m) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * m + 4 * grp + j;
@@ -642,27 +653,16 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
                 }
                 if (c16 == 0) my_st[r] = st;
             }
+        }
         if (tile < P.tiles_lossy) {
-            for (int slot = 0; slot < P.ppg; ++slot) {
-                const int first = slot * P.K;
-                const float inv = lossy_pos_inv_k(P, tile * (P.GR * P.ppg) + grp * P.ppg + slot);
+            float csum[G];
+#pragma unroll
+            for (int lam = 0; lam < 4 * MSUB; ++lam) {
                 float x[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    // head rows first .. first + K - 1 of this lane group, summed in head order
-                    float sum = 0.0f;
-#pragma unroll
-                    for (int lam = 0; lam < 4 * MSUB; ++lam) {
-                        const int i = lam - first;
-                        if (i >= 0 && i < P.K) {
-                            const float v = acc[g][lam >> 2][lam & 3];
-                            sum = i == 0 ? v : sum + v;
-                        }
-                    }
-                    x[g] = sum * inv;
-                }
-                const Stat st = row16_stat<G>(x, ok, col0);
-                if (c16 == 0) my_st[ROWS + grp * P.ppg + slot] = st;
+                for (int g = 0; g < G; ++g) x[g] = acc[g][lam >> 2][lam & 3];
+                centroid_slot<G>(P, lam, x, csum, ok, col0, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
+                                 &my_st[ROWS + grp * P.ppg]);
             }
         }
     }
