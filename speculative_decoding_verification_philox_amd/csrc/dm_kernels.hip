@@ -237,13 +237,15 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
 constexpr int kDppMirror = 0x140;      // row_mirror
 
+// Every lane of these patterns reads a lane of its own row, so bound_ctrl
+// changes nothing; it lets the compiler fold the move into the ALU op.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
 __device__ __forceinline__ float row16_max(float x) {
     x = fmaxf(x, dpp_f<kDppXor1>(x));
@@ -285,27 +287,92 @@ __device__ __forceinline__ Stat row16_stat(const float (&x)[G], const bool (&ok)
     return Stat{m, row16_sum(s), row16_min(idx)};
 }
 
-// Running centroid of the lossy positions in a lane group: slot lam of the
-// group is head i = lam mod K of position lam / K.  The head rows are summed
-// in head order as they go by (the order every kernel uses for the centroid,
-// see centroid_logit) and the position's statistics are taken at its last
-// head.  lam and K are uniform, so the branch is too.
-template <int G>
-__device__ __forceinline__ void centroid_slot(const Plan& P, int lam, const float (&x)[G], float (&csum)[G],
-                                              const bool (&ok)[G], int col0, int pos_base, bool write,
-                                              Stat* __restrict__ dst) {
-    const int slot = lam / P.K, i = lam - slot * P.K;
+// row16_stat for J rows at once: the J reductions are independent, so their
+// DPP steps interleave instead of each waiting on its own previous step.
+template <int J, int G>
+__device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (&ok)[G], int col0, Stat (&out)[J]) {
+    float m[J], s[J];
+    int idx[J];
 #pragma unroll
-    for (int g = 0; g < G; ++g) csum[g] = i == 0 ? x[g] : csum[g] + x[g];
-    if (i == P.K - 1 && slot < P.ppg) {
-        const float inv = lossy_pos_inv_k(P, pos_base + slot);
-        float xc[G];
+    for (int j = 0; j < J; ++j) {
+        m[j] = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < G; ++g) xc[g] = csum[g] * inv;
-        const Stat st = row16_stat<G>(xc, ok, col0);
-        if (write) dst[slot] = st;
+        for (int g = 0; g < G; ++g) m[j] = fmaxf(m[j], ok[g] ? x[j][g] : -INFINITY);
     }
+#pragma unroll
+    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppXor1>(m[j]));
+#pragma unroll
+    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppXor2>(m[j]));
+#pragma unroll
+    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppHalfMirror>(m[j]));
+#pragma unroll
+    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppMirror>(m[j]));
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        s[j] = 0.0f;
+        idx[j] = 0x7fffffff;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float e = __expf(x[j][g] - m[j]);
+            s[j] += ok[g] ? e : 0.0f;
+            idx[j] = (ok[g] && x[j][g] == m[j]) ? min(idx[j], col0 + 16 * g) : idx[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        s[j] = s[j] + dpp_f<kDppXor1>(s[j]);
+        idx[j] = min(idx[j], dpp_i<kDppXor1>(idx[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        s[j] = s[j] + dpp_f<kDppXor2>(s[j]);
+        idx[j] = min(idx[j], dpp_i<kDppXor2>(idx[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        s[j] = s[j] + dpp_f<kDppHalfMirror>(s[j]);
+        idx[j] = min(idx[j], dpp_i<kDppHalfMirror>(idx[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        s[j] = s[j] + dpp_f<kDppMirror>(s[j]);
+        idx[j] = min(idx[j], dpp_i<kDppMirror>(idx[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) out[j] = Stat{m[j], s[j], idx[j]};
 }
+
+// Running centroid of the lossy positions in a lane group: the group's head
+// slots are visited in order, slot lam being head i of position `slot` (i and
+// slot advance with lam, i wrapping at K; both uniform).  The head rows are
+// summed in head order as they go by (the order every kernel uses for the
+// centroid, see centroid_logit) and the position's statistics are taken at
+// its last head.  ACC(lam, g) yields the scaled row value of slot lam.
+#define DM_CENTROID_PASS(NSLOT, ACC, pos_base, write, dst)                          \
+    do {                                                                            \
+        float csum_[G];                                                             \
+        int i_ = 0, slot_ = 0;                                                      \
+        _Pragma("unroll") for (int lam_ = 0; lam_ < (NSLOT); ++lam_) {              \
+            if (i_ == 0) {                                                          \
+                _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) csum_[g_] = ACC(lam_, g_); \
+            } else {                                                                \
+                _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) csum_[g_] += ACC(lam_, g_); \
+            }                                                                       \
+            if (i_ == P.K - 1) {                                                    \
+                if (slot_ < P.ppg) {                                                \
+                    const float inv_ = lossy_pos_inv_k(P, (pos_base) + slot_);      \
+                    float xc_[G];                                                   \
+                    _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) xc_[g_] = csum_[g_] * inv_; \
+                    const Stat st_ = row16_stat<G>(xc_, ok, col0);                  \
+                    if (write) (dst)[slot_] = st_;                                  \
+                }                                                                   \
+                i_ = 0;                                                             \
+                ++slot_;                                                            \
+            } else {                                                                \
+                ++i_;                                                               \
+            }                                                                       \
+        }                                                                           \
+    } while (0)
 
 template <bool BF16, int MSUB>
 __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
@@ -384,42 +451,44 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
 #pragma unroll
     for (int g = 0; g < G; ++g) ok[g] = active && col0 + 16 * g < P.V;
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m)
+    for (int m = 0; m < MSUB; ++m) {
+        // the lane group's four rows of sub-tile m together
+        float sc[4], x[4][G];
+        int canon[4], store[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * m + 4 * grp + j;
-            const float sc = __shfl(my.scale, r, 64);
-            const int canon = __shfl(my.canon, r, 64);
-            const int store = __shfl(my.store, r, 64);
-            float x[G];
+            sc[j] = __shfl(my.scale, r, 64);
+            canon[j] = __shfl(my.canon, r, 64);
+            store[j] = __shfl(my.store, r, 64);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                x[g] = acc[g][m][j] * sc;
-                acc[g][m][j] = x[g];
+                x[j][g] = acc[g][m][j] * sc[j];
+                acc[g][m][j] = x[j][g];
             }
-            Stat st = stat_empty();
-            if (canon >= 0) {  // not a padding row (the whole 16-lane row agrees)
-                if (store) {
 #pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        if (ok[g]) logits[(size_t)canon * P.V + col0 + 16 * g] = x[g];
-                }
-                st = row16_stat<G>(x, ok, col0);
+        for (int j = 0; j < 4; ++j)
+            if (canon[j] >= 0 && store[j]) {  // the whole 16-lane row agrees
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if (ok[g]) logits[(size_t)canon[j] * P.V + col0 + 16 * g] = x[j][g];
             }
-            if (c == 0) s_st[wave][r] = st;
+        Stat st[4];
+        row16_stats<4, G>(x, ok, col0, st);
+        if (c == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_st[wave][16 * m + 4 * grp + j] = canon[j] >= 0 ? st[j] : stat_empty();
         }
+    }
     const int npt = P.GR * P.ppg;
     const bool lossy_tile = tile < P.tiles_lossy;
     if (lossy_tile) {
-        float csum[G];
-#pragma unroll
-        for (int lam = 0; lam < 4 * MSUB; ++lam) {
-            float x[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) x[g] = acc[g][lam >> 2][lam & 3];
-            centroid_slot<G>(P, lam, x, csum, ok, col0, tile * npt + grp * P.ppg, c == 0,
-                             &s_st[wave][ROWS + grp * P.ppg]);
-        }
+#define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
+        DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
+#undef DM_ACC
     }
     __syncthreads();
     // merge the workgroup's panels in panel order: part[target][panel group]
@@ -632,38 +701,38 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
         for (int g = 0; g < G; ++g) ok[g] = my_panel < P.n_panels && col0 + 16 * g < P.V;
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) {
+            // the lane group's four rows of sub-tile m: metadata read together,
+            // statistics reduced together
+            RowMeta mt[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * m + 4 * grp + j;
-                const RowMeta mt = my_meta[r];
-                float x[G];
+            for (int j = 0; j < 4; ++j) mt[j] = my_meta[16 * m + 4 * grp + j];
+            float x[4][G];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    x[g] = acc[g][m][j] * mt.scale;
-                    acc[g][m][j] = x[g];
+                    x[j][g] = acc[g][m][j] * mt[j].scale;
+                    acc[g][m][j] = x[j][g];
                 }
-                Stat st = stat_empty();
-                if (mt.canon >= 0) {  // not a padding row (the whole 16-lane row agrees)
-                    if (mt.store) {
 #pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            if (ok[g]) logits[(size_t)mt.canon * P.V + col0 + 16 * g] = x[g];
-                    }
-                    st = row16_stat<G>(x, ok, col0);
+            for (int j = 0; j < 4; ++j)
+                if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        if (ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
                 }
-                if (c16 == 0) my_st[r] = st;
+            Stat st[4];
+            row16_stats<4, G>(x, ok, col0, st);
+            if (c16 == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) my_st[16 * m + 4 * grp + j] = mt[j].canon >= 0 ? st[j] : stat_empty();
             }
         }
         if (tile < P.tiles_lossy) {
-            float csum[G];
-#pragma unroll
-            for (int lam = 0; lam < 4 * MSUB; ++lam) {
-                float x[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) x[g] = acc[g][lam >> 2][lam & 3];
-                centroid_slot<G>(P, lam, x, csum, ok, col0, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
-                                 &my_st[ROWS + grp * P.ppg]);
-            }
+#define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
+            DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
+                             &my_st[ROWS + grp * P.ppg]);
+#undef DM_ACC
         }
     }
     __syncthreads();
