@@ -182,23 +182,32 @@ def test_output_histogram_small_vocab_gpu():
 
 # ------------------------------------------------------------ the limits
 def test_maximum_batch_gamma_and_heads(layout):
-    """max_batch = 256, gamma = 31 (32 positions), K = 16, all three rules;
-    the oracle checks a sample of sequences (a sequence's outputs depend only
-    on its own rows)."""
+    """max_batch = 256, gamma = 63 (64 positions, one wave), K = 16, all four
+    rules (every fourth sequence a 63-node tree); the oracle checks a sample
+    of sequences (a sequence's outputs depend only on its own rows)."""
     import torch
 
-    w = wl.generate(2, B=256, gamma=31, d=64, V=700, K=16, planted=0.6)
-    modes = (np.arange(256) % 3).astype(np.uint8)
+    w = wl.generate(2, B=256, gamma=63, d=64, V=700, K=16, planted=0.6)
+    modes = (np.arange(256) % 4).astype(np.uint8)
+    rng = np.random.default_rng(63)
+    tree = np.stack([wl.tree_parents(rng, 63, 8) for _ in range(256)])
     ver = P.make_verifier(w.W, w.h, 16)
     inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
-    seqs = np.array([0, 1, 2, 77, 128, 200, 254, 255], np.int32)
+    seqs = np.array([0, 1, 2, 3, 77, 128, 200, 203, 254, 255], np.int32)
     for seed in (3, 2**40 + 5):
-        print(f"  B=256 gamma=31 K=16 seed={seed} layout={layout}", flush=True)
-        g = P.run_gpu(ver, inp, modes, 16, 0.3, seed, layout=layout)
-        o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, modes, 16, 0.3, seed, seqs=seqs)
+        print(f"  B=256 gamma=63 K=16 seed={seed} layout={layout}", flush=True)
+        g = P.run_gpu(ver, inp, modes, 16, 0.3, seed, layout=layout, tree=tree)
+        o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, modes, 16, 0.3, seed, seqs=seqs, tree=tree)
         P.compare(g, o, modes, 16, seqs=seqs)
     ver.close()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d,V", [(65536, 1024), (64, 524288)], ids=["widest_hidden", "largest_vocab"])
+def test_widest_hidden_and_largest_vocabulary(d, V, layout):
+    """The descriptor's limits on d and |V|, every rule."""
+    w = wl.generate(2, B=3, gamma=2, d=d, V=V, K=2, planted=0.9)
+    _check(w.W, w.h, w.draft, w.q_hat, np.array([0, 1, 2], np.uint8), 2, 0.2, [5], layout=layout)
 
 
 @pytest.mark.parametrize("V", [1, 2, 63, 65])
