@@ -53,7 +53,8 @@
  *     2)[v%4] >> 9) + 1/2) * 2^-23, ties to the smallest v.
  *
  *   Philox is Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed
- *   (low word first).  A draft id outside [0, vocab) is rejected.
+ *   (low word first).  A draft id outside [0, vocab) is rejected, and so is
+ *   a draft whose tree parent is out of range; data_status reports both.
  *
  * Precision: bf16 (or fp32) inputs, fp32 accumulation and statistics.
  *
@@ -159,6 +160,9 @@ typedef struct dm_verify_args {
     int32_t* out_token;     /* device out [B]: correction (A < gamma) or bonus (A == gamma) token */
     int32_t* accept_pos;    /* device out [B] or NULL: position of the last kept node, whose p-bar
                                (or p) gave out_token; A for chains */
+    uint32_t* data_status;  /* device out [B] or NULL: what the device found in the sequence's own
+                               inputs (each such draft was rejected): bit 0 a draft id outside
+                               [0, vocab), bit 1 a tree parent outside [0, t]; 0 = none */
     /* Optional device outputs for inspection; NULL = not written. */
     uint8_t* accept_flags;     /* [B, gamma] decision at every drafted position */
     int32_t* head_argmax;      /* [B, gamma+1, K]; -1 in heads 1.. of lossless sequences */

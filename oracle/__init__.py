@@ -51,6 +51,7 @@ class _Result(ctypes.Structure):
         ("js_heads", _c_f64p), ("js_draft", _c_f64p), ("logits", _c_f64p),
         ("mask_bits", _c_u32p), ("race_gap", _c_f64p), ("filter_count", _c_i32p),
         ("filter_logz", _c_f64p), ("filter_margin", _c_f64p), ("accept_pos", _c_i32p),
+        ("data_status", _c_u32p),
     ]
 
 
@@ -235,6 +236,7 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
     out = {
         "accept_len": np.full(n, -1, np.int32),
         "accept_pos": np.full(n, -1, np.int32),
+        "data_status": np.zeros(n, np.uint32),
         "out_token": np.full(n, -1, np.int32),
         "accept_flags": np.zeros((n, G), np.uint8),
         "margin": np.full((n, G), np.nan),

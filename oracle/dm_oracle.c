@@ -411,6 +411,8 @@ typedef struct dmo_result { /* leading dimension n_seq everywhere; NULL = not wa
     double* filter_logz;      /* [n, gamma+1] lossless sequences: log sum over S of e^l */
     double* filter_margin;    /* [n, gamma+1] lossless sequences: see dmo_processed */
     int32_t* accept_pos;      /* [n] position of the last kept node (chains: accept_len) */
+    uint32_t* data_status;    /* [n] bit 0: a draft id outside [0, vocab); bit 1: a tree parent
+                                 outside [0, t] (each such draft counts as rejected) */
 } dmo_result;
 
 /* ------------------------------------------------------------------------ */
@@ -542,10 +544,12 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
         }
 
         /* Decisions for every drafted position t < gamma_b. */
+        uint32_t status = 0;
         for (int t = 0; t < Gb; ++t) {
             const int32_t x = P->draft[(size_t)b * G + t];
             const uint32_t pidx = (uint32_t)(b * T1 + t);
             const int valid = x >= 0 && x < V;
+            if (!valid) status |= 1u;
             int accept = 0;
             double margin = INFINITY;
             double min_gap = INFINITY;
@@ -557,6 +561,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
             } else if (mode == DMO_TREE_NAIVE) {
                 /* [TR]: draft t is judged by the heads at its parent position */
                 const int32_t up = P->tree_parent[(size_t)b * G + t];
+                if (!(up >= 0 && up <= t)) status |= 2u;
                 if (up >= 0 && up <= t) {
                     accept = valid && dmo_rule_naive(rarg + up * K, rows, x);
                     margin = INFINITY;
@@ -661,6 +666,7 @@ int dmo_run(const dmo_problem* P, const dmo_result* R)
 
         if (R->accept_len) R->accept_len[n] = A;
         if (R->accept_pos) R->accept_pos[n] = pos;
+        if (R->data_status) R->data_status[n] = status;
         if (R->out_token) R->out_token[n] = y;
         if (R->race_gap) R->race_gap[n] = race_gap;
         for (int t = 0; t < T1; ++t) {

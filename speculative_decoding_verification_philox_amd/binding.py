@@ -43,7 +43,7 @@ class dm_verify_args(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("reserved", ctypes.c_uint32),
         ("seq_gamma", ctypes.c_void_p), ("seq_heads", ctypes.c_void_p), ("seq_p_drop", ctypes.c_void_p),
         ("tree_parent", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("out_token", ctypes.c_void_p),
-        ("accept_pos", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
+        ("accept_pos", ctypes.c_void_p), ("data_status", ctypes.c_void_p), ("accept_flags", ctypes.c_void_p), ("head_argmax", ctypes.c_void_p),
         ("centroid_argmax", ctypes.c_void_p), ("head_logz", ctypes.c_void_p), ("centroid_logz", ctypes.c_void_p),
         ("js_heads", ctypes.c_void_p), ("js_draft", ctypes.c_void_p), ("logits", ctypes.c_void_p),
         ("mask_bits", ctypes.c_void_p), ("filter_count", ctypes.c_void_p), ("filter_logz", ctypes.c_void_p),
@@ -194,7 +194,7 @@ class Verifier:
 
     def make_args(self, W, h, draft, q_hat, modes, K, p_drop, seed, accept_len, out_token, w_layout=DM_W_ROW_MAJOR,
                   temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None, seq_p_drop=None,
-                  tree_parent=None, accept_pos=None, **debug):
+                  tree_parent=None, accept_pos=None, data_status=None, **debug):
         import torch
 
         D = self.desc
@@ -241,6 +241,8 @@ class Verifier:
         a.out_token = self._expect("out_token", out_token, (B,), torch.int32, dev)
         if accept_pos is not None:
             a.accept_pos = self._expect("accept_pos", accept_pos, (B,), torch.int32, dev)
+        if data_status is not None:
+            a.data_status = self._expect("data_status", data_status, (B,), torch.int32, dev)
         shapes = {"accept_flags": ((B, G), torch.uint8), "head_argmax": ((B, T1, K), torch.int32),
                   "centroid_argmax": ((B, T1), torch.int32), "head_logz": ((B, T1, K), torch.float32),
                   "centroid_logz": ((B, T1), torch.float32), "js_heads": ((B, G, K), torch.float32),
@@ -267,8 +269,8 @@ class Verifier:
         target.  seq_gamma / seq_heads / seq_p_drop (host arrays of B, or
         None) make the batch ragged.  tree_parent (device int32 [B, gamma])
         gives the parent position of every draft of the TREE_NAIVE
-        sequences.  Returns a dict with accept_len, accept_pos and out_token
-        (and every debug output when debug=True).  Preallocated outputs can
+        sequences.  Returns a dict with accept_len, accept_pos, out_token and
+        data_status (and every debug output when debug=True).  Preallocated outputs can
         be passed in `outputs`."""
         import torch
 
@@ -280,6 +282,7 @@ class Verifier:
         out.setdefault("accept_len", torch.empty(B, dtype=torch.int32, device=dev))
         out.setdefault("out_token", torch.empty(B, dtype=torch.int32, device=dev))
         out.setdefault("accept_pos", torch.empty(B, dtype=torch.int32, device=dev))
+        out.setdefault("data_status", torch.empty(B, dtype=torch.int32, device=dev))  # uint32 bits
         if debug:
             out.setdefault("accept_flags", torch.zeros((B, G), dtype=torch.uint8, device=dev))
             out.setdefault("head_argmax", torch.empty((B, T1, K), dtype=torch.int32, device=dev))
@@ -297,7 +300,8 @@ class Verifier:
         args = self.make_args(W, h, draft, q_hat, modes, K, p_drop, seed, out["accept_len"], out["out_token"],
                               w_layout=w_layout, temperature=temperature, top_k=top_k, top_p=top_p,
                               seq_gamma=seq_gamma, seq_heads=seq_heads, seq_p_drop=seq_p_drop,
-                              tree_parent=tree_parent, accept_pos=out["accept_pos"], **dbg)
+                              tree_parent=tree_parent, accept_pos=out["accept_pos"],
+                              data_status=out["data_status"], **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         dm_verify_run(self.handle, args, stream)

@@ -1388,6 +1388,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                                                            int32_t* __restrict__ accept_len,
                                                            int32_t* __restrict__ out_token,
                                                            int32_t* __restrict__ accept_pos,
+                                                           uint32_t* __restrict__ data_status,
                                                            uint8_t* __restrict__ dbg_flags,
                                                            float* __restrict__ dbg_js_heads,
                                                            float* __restrict__ dbg_js_draft) {
@@ -1477,6 +1478,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
         }
         if (dbg_flags) dbg_flags[b * G + lane] = accept ? 1 : 0;
     }
+    // inputs the device found out of range (each such draft was rejected)
+    const bool bad_draft = lane < Gb && !(x >= 0 && x < P.V);
+    const bool bad_parent = tree && lane < Gb && !(up >= 0 && up <= lane);
+    const unsigned long long any_bad_draft = __ballot(bad_draft), any_bad_parent = __ballot(bad_parent);
     int A, pos;
     if (tree) {
         A = tree_walk(lane < Gb, accept, up, lane, &pos);
@@ -1488,6 +1493,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
     if (lane == 0) {
         accept_len[b] = A;
         if (accept_pos) accept_pos[b] = pos;
+        if (data_status) data_status[b] = (any_bad_draft ? 1u : 0u) | (any_bad_parent ? 2u : 0u);
         if (lossless) {
             const unsigned long long best = best_r ? best_r : best_p;
             out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
@@ -1962,8 +1968,8 @@ hipError_t launch_filter(const Plan& P, const float* logits, const RowStat* rows
 hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const int32_t* tree_parent,
                         const float* logits, const RowStat* rowstat, const RowStat* centstat, float* jspart,
                         unsigned long long* race_best, const FiltStat* filt, int32_t* accept_len, int32_t* out_token,
-                        int32_t* accept_pos, uint8_t* dbg_flags, float* dbg_js_heads, float* dbg_js_draft,
-                        hipStream_t st) {
+                        int32_t* accept_pos, uint32_t* data_status, uint8_t* dbg_flags, float* dbg_js_heads,
+                        float* dbg_js_draft, hipStream_t st) {
     if (P.blk_js + P.blk_race > 0) {
         hipLaunchKernelGGL(k_vocab, dim3(P.blk_js + P.blk_race), dim3(kVocabThreads), 0, st, P, draft, q_hat, logits,
                            rowstat, centstat, jspart, race_best, filt);
@@ -1971,8 +1977,8 @@ hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat,
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_finish, dim3(P.B), dim3(kFinishThreads), 0, st, P, draft, q_hat, tree_parent, logits,
-                       rowstat, centstat, jspart, race_best, filt, accept_len, out_token, accept_pos, dbg_flags,
-                       dbg_js_heads, dbg_js_draft);
+                       rowstat, centstat, jspart, race_best, filt, accept_len, out_token, accept_pos, data_status,
+                       dbg_flags, dbg_js_heads, dbg_js_draft);
     return hipGetLastError();
 }
 

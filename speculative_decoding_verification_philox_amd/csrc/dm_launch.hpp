@@ -18,8 +18,8 @@ hipError_t launch_filter(const Plan& P, const float* logits, const RowStat* rows
 hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const int32_t* tree_parent,
                         const float* logits, const RowStat* rowstat, const RowStat* centstat, float* jspart,
                         unsigned long long* race_best, const FiltStat* filt, int32_t* accept_len, int32_t* out_token,
-                        int32_t* accept_pos, uint8_t* dbg_flags, float* dbg_js_heads, float* dbg_js_draft,
-                        hipStream_t st);
+                        int32_t* accept_pos, uint32_t* data_status, uint8_t* dbg_flags, float* dbg_js_heads,
+                        float* dbg_js_draft, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 
 // Vocabulary strips (16 rows each) one workgroup of the skinny GEMM covers.

@@ -93,7 +93,7 @@ int check_args(const dm_verify_desc* D, const dm_verify_args* a) {
     if (!aligned(a->W, 16) || !aligned(a->h, 16)) return DM_ERR_UNSUPPORTED;
     const void* four[] = {a->draft, a->q_hat, a->accept_len, a->out_token, a->head_argmax, a->centroid_argmax,
                           a->head_logz, a->centroid_logz, a->js_heads, a->js_draft, a->logits, a->mask_bits,
-                          a->filter_count, a->filter_logz, a->tree_parent, a->accept_pos};
+                          a->filter_count, a->filter_logz, a->tree_parent, a->accept_pos, a->data_status};
     for (const void* p : four)
         if (p && !aligned(p, 4)) return DM_ERR_UNSUPPORTED;
     return DM_OK;
@@ -445,8 +445,8 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
                           a->centroid_logz, st));
     DM_TRY(launch_filter(P, logits, h->rowstat, h->filt, a->filter_count, a->filter_logz, st));
     DM_TRY(launch_vocab(P, a->draft, a->q_hat, a->tree_parent, logits, h->rowstat, h->centstat, h->jspart, h->race,
-                        h->filt, a->accept_len, a->out_token, a->accept_pos, a->accept_flags, a->js_heads,
-                        a->js_draft, st));
+                        h->filt, a->accept_len, a->out_token, a->accept_pos, a->data_status, a->accept_flags,
+                        a->js_heads, a->js_draft, st));
 #undef DM_TRY
     return DM_OK;
 }

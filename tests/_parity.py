@@ -214,6 +214,9 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False, rag
             bad = gf != of
             assert np.all(near[bad]), f"decision mismatch of sequence {b} at positions {np.nonzero(bad & ~near)[0]}"
             rep.decision_mismatch_exempt += int(bad.sum())
+        if "data_status" in gpu:  # integer work on the inputs: always exact
+            assert int(gpu["data_status"][b]) == int(ora["data_status"][r]), (
+                f"data_status of sequence {b}: gpu {gpu['data_status'][b]} oracle {ora['data_status'][r]}")
         # accepted length and emitted token
         A_o = int(ora["accept_len"][r])
         rep.sequences += 1

@@ -21,7 +21,7 @@ hipError_t launch_filter(const Plan&, const float*, const RowStat*, FiltStat*, i
 }
 hipError_t launch_vocab(const Plan&, const int32_t*, const float*, const int32_t*, const float*, const RowStat*,
                         const RowStat*, float*, unsigned long long*, const FiltStat*, int32_t*, int32_t*, int32_t*,
-                        uint8_t*, float*, float*, hipStream_t) {
+                        uint32_t*, uint8_t*, float*, float*, hipStream_t) {
     return hipSuccess;
 }
 hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipSuccess; }

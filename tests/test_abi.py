@@ -48,11 +48,12 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header(lib):
     # sizes follow from the field lists in include/dm_verify.h on LP64
     assert ctypes.sizeof(B.dm_verify_desc) == 24
-    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 4 * 8 + 3 * 8 + 11 * 8
+    assert ctypes.sizeof(B.dm_verify_args) == 5 * 8 + 4 * 4 + 8 + 4 * 4 + 4 * 8 + 4 * 8 + 11 * 8
     assert B.dm_verify_args.seed.offset == 56
     assert B.dm_verify_args.temperature.offset == 64 and B.dm_verify_args.seq_gamma.offset == 80
     assert B.dm_verify_args.tree_parent.offset == 104 and B.dm_verify_args.accept_len.offset == 112
-    assert B.dm_verify_args.accept_pos.offset == 128 and B.dm_verify_args.accept_flags.offset == 136
+    assert B.dm_verify_args.accept_pos.offset == 128 and B.dm_verify_args.data_status.offset == 136
+    assert B.dm_verify_args.accept_flags.offset == 144
 
 
 def desc(**kw):
@@ -135,6 +136,7 @@ def test_bad_desc(lib, field, value, status):
     (dict(reserved=1), B.DM_ERR_INVALID_ARGUMENT),
     (dict(filter_count=0x10002), B.DM_ERR_UNSUPPORTED),
     (dict(accept_pos=0x10002), B.DM_ERR_UNSUPPORTED),
+    (dict(data_status=0x10002), B.DM_ERR_UNSUPPORTED),
     (dict(modes=(3, 1), tree_parent=0x10002), B.DM_ERR_UNSUPPORTED),
     (dict(seq_gamma=[5, 0]), B.DM_ERR_INVALID_ARGUMENT),
     (dict(seq_gamma=[-1, 0]), B.DM_ERR_INVALID_ARGUMENT),

@@ -269,3 +269,25 @@ def test_tree_needs_parents():
         _run(w, np.full(2, TREE, np.uint8), 2, 0.1, None)
     with pytest.raises(RuntimeError):
         _run(w, np.full(2, 4, np.uint8), 2, 0.1, None)
+
+
+def test_data_status_flags_bad_drafts_and_parents():
+    """Bit 0: a draft id outside [0, V); bit 1: a tree parent outside [0, t];
+    only the sequence's own drafts (t < gamma_b) count."""
+    w = wl.generate(0, seed_base=21, B=4, gamma=5, d=64, V=200, K=2, planted=0.8)
+    B, G = w.draft.shape
+    par = np.tile(np.arange(G, dtype=np.int32), (B, 1))
+    w.draft[1, 2] = 200
+    w.draft[3, 4] = -1
+    par[2, 3] = 4
+    par[3, 0] = -7
+    modes = np.array([TREE, TREE, TREE, TREE], np.uint8)
+    r = _run(w, modes, 2, 0.1, par)
+    np.testing.assert_array_equal(r["data_status"], [0, 1, 2, 3])
+    assert not r["accept_flags"][1, 2] and not r["accept_flags"][2, 3] and not r["accept_flags"][3, 0]
+    # past a ragged sequence's drafts nothing is read
+    r = _run(w, modes, 2, 0.1, par, seq_gamma=np.array([5, 2, 3, 0], np.int32))
+    np.testing.assert_array_equal(r["data_status"], [0, 0, 0, 0])
+    # chains: only the draft ids
+    r = _run(w, np.full(B, oracle.NAIVE, np.uint8), 2, 0.1, par)
+    np.testing.assert_array_equal(r["data_status"], [0, 1, 0, 1])
