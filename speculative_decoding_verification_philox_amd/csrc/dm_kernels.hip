@@ -247,18 +247,6 @@ template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
     return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp_f<kDppXor1>(x));
-    x = fmaxf(x, dpp_f<kDppXor2>(x));
-    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-    return fmaxf(x, dpp_f<kDppMirror>(x));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x = x + dpp_f<kDppXor1>(x);
-    x = x + dpp_f<kDppXor2>(x);
-    x = x + dpp_f<kDppHalfMirror>(x);
-    return x + dpp_f<kDppMirror>(x);
-}
 __device__ __forceinline__ int row16_min(int x) {
     x = min(x, dpp_i<kDppXor1>(x));
     x = min(x, dpp_i<kDppXor2>(x));
@@ -266,56 +254,73 @@ __device__ __forceinline__ int row16_min(int x) {
     return min(x, dpp_i<kDppMirror>(x));
 }
 
-// (max, sum exp, lowest argmax) of the 64 values held as four per lane by
-// the 16 lanes of a row; columns >= V are left out.  Selects instead of
-// branches: a left-out column adds exactly 0 to the sum and -inf to the max,
-// so the result is the same as skipping it.
-template <int G>
-__device__ __forceinline__ Stat row16_stat(const float (&x)[G], const bool (&ok)[G], int col0) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < G; ++g) m = fmaxf(m, ok[g] ? x[g] : -INFINITY);
-    m = row16_max(m);
-    float s = 0.0f;
-    int idx = 0x7fffffff;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float e = __expf(x[g] - m);
-        s += ok[g] ? e : 0.0f;
-        idx = (ok[g] && x[g] == m) ? min(idx, col0 + 16 * g) : idx;
-    }
-    return Stat{m, row16_sum(s), row16_min(idx)};
-}
+constexpr float kLog2e = 1.44269504088896341f;
 
-// row16_stat for J rows at once: the J reductions are independent, so their
-// DPP steps interleave instead of each waiting on its own previous step.
-template <int J, int G>
+// A compile-time bool carried as an argument, so one generic lambda gives
+// two specialised epilogues.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
+// Order-preserving map from a float's bits to a signed integer, its own
+// inverse: on non-NaN values integer order is float order (-0 sorts just
+// below +0, and the two compare equal afterwards).  The 16-lane max runs on
+// these keys because the integer max takes the DPP lane move as an operand
+// modifier, where a float max would first quiet a possible NaN.
+__device__ __forceinline__ int fkey(float x) {
+    const int b = __float_as_int(x);
+    return b ^ (int)((uint32_t)(b >> 31) >> 1);
+}
+__device__ __forceinline__ float fkey_inv(int k) { return __int_as_float(k ^ (int)((uint32_t)(k >> 31) >> 1)); }
+
+// (max, sum exp, lowest argmax) of J rows, each held as G values per lane by
+// the 16 lanes of a DPP row (lane c holds columns col0 + 16 g); the J
+// reductions are independent, so their DPP steps interleave.
+//
+// FULL: every column is a vocabulary entry, so no lane-out test is needed
+// and the values are finite; e^(x - m) is taken as 2^(x log2 e - m log2 e).
+// Otherwise columns with ok[g] false are left out by selects (they add
+// exactly 0 to the sum and -inf to the max), and a row with no column at all
+// gives the empty statistic.
+template <int J, int G, bool FULL>
 __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (&ok)[G], int col0, Stat (&out)[J]) {
     float m[J], s[J];
-    int idx[J];
+    int k[J], idx[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        m[j] = -INFINITY;
+        float mm = (FULL || ok[0]) ? x[j][0] : -INFINITY;
 #pragma unroll
-        for (int g = 0; g < G; ++g) m[j] = fmaxf(m[j], ok[g] ? x[j][g] : -INFINITY);
+        for (int g = 1; g < G; ++g) mm = fmaxf(mm, (FULL || ok[g]) ? x[j][g] : -INFINITY);
+        k[j] = fkey(mm);
     }
 #pragma unroll
-    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppXor1>(m[j]));
+    for (int j = 0; j < J; ++j) k[j] = max(k[j], dpp_i<kDppXor1>(k[j]));
 #pragma unroll
-    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppXor2>(m[j]));
+    for (int j = 0; j < J; ++j) k[j] = max(k[j], dpp_i<kDppXor2>(k[j]));
 #pragma unroll
-    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppHalfMirror>(m[j]));
+    for (int j = 0; j < J; ++j) k[j] = max(k[j], dpp_i<kDppHalfMirror>(k[j]));
 #pragma unroll
-    for (int j = 0; j < J; ++j) m[j] = fmaxf(m[j], dpp_f<kDppMirror>(m[j]));
+    for (int j = 0; j < J; ++j) k[j] = max(k[j], dpp_i<kDppMirror>(k[j]));
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+        m[j] = fkey_inv(k[j]);
         s[j] = 0.0f;
         idx[j] = 0x7fffffff;
+        if (FULL) {
+            const float ml = m[j] * kLog2e;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float e = __expf(x[j][g] - m[j]);
-            s[j] += ok[g] ? e : 0.0f;
-            idx[j] = (ok[g] && x[j][g] == m[j]) ? min(idx[j], col0 + 16 * g) : idx[j];
+            for (int g = 0; g < G; ++g) s[j] += __builtin_amdgcn_exp2f(fmaf(x[j][g], kLog2e, -ml));
+            // the lowest column attaining the max: the last write is the smallest g
+#pragma unroll
+            for (int g = G - 1; g >= 0; --g) idx[j] = x[j][g] == m[j] ? col0 + 16 * g : idx[j];
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float e = __expf(x[j][g] - m[j]);
+                s[j] += ok[g] ? e : 0.0f;
+                idx[j] = (ok[g] && x[j][g] == m[j]) ? min(idx[j], col0 + 16 * g) : idx[j];
+            }
         }
     }
 #pragma unroll
@@ -361,10 +366,11 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
             if (i_ == P.K - 1) {                                                    \
                 if (slot_ < P.ppg) {                                                \
                     const float inv_ = lossy_pos_inv_k(P, (pos_base) + slot_);      \
-                    float xc_[G];                                                   \
-                    _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) xc_[g_] = csum_[g_] * inv_; \
-                    const Stat st_ = row16_stat<G>(xc_, ok, col0);                  \
-                    if (write) (dst)[slot_] = st_;                                  \
+                    float xc_[1][G];                                                \
+                    _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) xc_[0][g_] = csum_[g_] * inv_; \
+                    Stat st_[1];                                                    \
+                    row16_stats<1, G, FULL>(xc_, ok, col0, st_);                    \
+                    if (write) (dst)[slot_] = st_[0];                               \
                 }                                                                   \
                 i_ = 0;                                                             \
                 ++slot_;                                                            \
@@ -450,46 +456,55 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
     bool ok[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) ok[g] = active && col0 + 16 * g < P.V;
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-        // the lane group's four rows of sub-tile m together
-        float sc[4], x[4][G];
-        int canon[4], store[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * m + 4 * grp + j;
-            sc[j] = __shfl(my.scale, r, 64);
-            canon[j] = __shfl(my.canon, r, 64);
-            store[j] = __shfl(my.store, r, 64);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                x[j][g] = acc[g][m][j] * sc[j];
-                acc[g][m][j] = x[j][g];
-            }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (canon[j] >= 0 && store[j]) {  // the whole 16-lane row agrees
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    if (ok[g]) logits[(size_t)canon[j] * P.V + col0 + 16 * g] = x[j][g];
-            }
-        Stat st[4];
-        row16_stats<4, G>(x, ok, col0, st);
-        if (c == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s_st[wave][16 * m + 4 * grp + j] = canon[j] >= 0 ? st[j] : stat_empty();
-        }
-    }
     const int npt = P.GR * P.ppg;
     const bool lossy_tile = tile < P.tiles_lossy;
-    if (lossy_tile) {
+    // FULL: the panel lies wholly inside the vocabulary (every panel but
+    // possibly the last), so its statistics need no per-column selects
+    auto epilogue = [&](auto full) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) {
+            // the lane group's four rows of sub-tile m together
+            float sc[4], x[4][G];
+            int canon[4], store[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * m + 4 * grp + j;
+                sc[j] = __shfl(my.scale, r, 64);
+                canon[j] = __shfl(my.canon, r, 64);
+                store[j] = __shfl(my.store, r, 64);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    x[j][g] = acc[g][m][j] * sc[j];
+                    acc[g][m][j] = x[j][g];
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (canon[j] >= 0 && store[j]) {  // the whole 16-lane row agrees
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        if (FULL || ok[g]) logits[(size_t)canon[j] * P.V + col0 + 16 * g] = x[j][g];
+                }
+            Stat st[4];
+            row16_stats<4, G, FULL>(x, ok, col0, st);
+            if (c == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_st[wave][16 * m + 4 * grp + j] = canon[j] >= 0 ? st[j] : stat_empty();
+            }
+        }
+        if (lossy_tile) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-        DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
+            DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
 #undef DM_ACC
-    }
+        }
+    };
+    if (active && (panel + 1) * 64 <= P.V)
+        epilogue(BoolTag<true>{});
+    else
+        epilogue(BoolTag<false>{});
     __syncthreads();
     // merge the workgroup's panels in panel order: part[target][panel group]
     const int nloc = ROWS + (lossy_tile ? npt : 0);
@@ -699,41 +714,50 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
         bool ok[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) ok[g] = my_panel < P.n_panels && col0 + 16 * g < P.V;
+        // FULL: the panel lies wholly inside the vocabulary (no per-column selects)
+        auto epilogue = [&](auto full) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
-            // the lane group's four rows of sub-tile m: metadata read together,
-            // statistics reduced together
-            RowMeta mt[4];
+            for (int m = 0; m < MSUB; ++m) {
+                // the lane group's four rows of sub-tile m: metadata read together,
+                // statistics reduced together
+                RowMeta mt[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mt[j] = my_meta[16 * m + 4 * grp + j];
-            float x[4][G];
+                for (int j = 0; j < 4; ++j) mt[j] = my_meta[16 * m + 4 * grp + j];
+                float x[4][G];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    x[j][g] = acc[g][m][j] * mt[j].scale;
-                    acc[g][m][j] = x[j][g];
+                    for (int g = 0; g < G; ++g) {
+                        x[j][g] = acc[g][m][j] * mt[j].scale;
+                        acc[g][m][j] = x[j][g];
+                    }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            if (FULL || ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
+                    }
+                Stat st[4];
+                row16_stats<4, G, FULL>(x, ok, col0, st);
+                if (c16 == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        my_st[16 * m + 4 * grp + j] = mt[j].canon >= 0 ? st[j] : stat_empty();
                 }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        if (ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
-                }
-            Stat st[4];
-            row16_stats<4, G>(x, ok, col0, st);
-            if (c16 == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) my_st[16 * m + 4 * grp + j] = mt[j].canon >= 0 ? st[j] : stat_empty();
             }
-        }
-        if (tile < P.tiles_lossy) {
+            if (tile < P.tiles_lossy) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-            DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
-                             &my_st[ROWS + grp * P.ppg]);
+                DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
+                                 &my_st[ROWS + grp * P.ppg]);
 #undef DM_ACC
-        }
+            }
+        };
+        if (my_panel < P.n_panels && (my_panel + 1) * 64 <= P.V)
+            epilogue(BoolTag<true>{});
+        else
+            epilogue(BoolTag<false>{});
     }
     __syncthreads();
     // merge the four panels in panel order: part[target][panel group]
@@ -1088,7 +1112,6 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // e^x and ln x on the hardware base-2 units (v_exp_f32, v_log_f32), for
 // arguments whose results stay in the normal fp32 range.
-constexpr float kLog2e = 1.44269504088896341f;
 __device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float hw_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
