@@ -380,8 +380,46 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
         }                                                                           \
     } while (0)
 
+// The same pass with the head count KC fixed at compile time: a position's
+// KC slots are summed in head order exactly as above, and then the
+// statistics of all NSLOT / KC positions of the lane group are reduced
+// together, so their DPP steps interleave instead of running one position
+// after another.
+#define DM_CENTROID_K(KC, NSLOT, ACC, pos_base, write, dst)                        \
+    do {                                                                           \
+        constexpr int NP_ = (NSLOT) / (KC);                                        \
+        if constexpr (NP_ > 0) {                                                   \
+            float xc_[NP_ > 0 ? NP_ : 1][G];                                       \
+            _Pragma("unroll") for (int p_ = 0; p_ < NP_; ++p_) {                    \
+                const float inv_ = lossy_pos_inv_k(P, (pos_base) + p_);             \
+                _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) {                 \
+                    float s_ = ACC(p_ * (KC), g_);                                  \
+                    _Pragma("unroll") for (int i_ = 1; i_ < (KC); ++i_) s_ += ACC(p_ * (KC) + i_, g_); \
+                    xc_[p_][g_] = s_ * inv_;                                        \
+                }                                                                  \
+            }                                                                      \
+            Stat st_[NP_ > 0 ? NP_ : 1];                                           \
+            row16_stats<NP_, G, FULL>(xc_, ok, col0, st_);                          \
+            if (write) {                                                           \
+                _Pragma("unroll") for (int p_ = 0; p_ < NP_; ++p_) (dst)[p_] = st_[p_]; \
+            }                                                                      \
+        }                                                                          \
+    } while (0)
+
+// Centroid statistics of a lane group: the common head counts take the
+// interleaved pass on full panels, every other case the running one.
+#define DM_CENTROIDS(NSLOT, ACC, pos_base, write, dst)                             \
+    do {                                                                           \
+        if (FULL && P.K == 5)                                                      \
+            DM_CENTROID_K(5, NSLOT, ACC, pos_base, write, dst);                     \
+        else if (FULL && P.K == 8)                                                 \
+            DM_CENTROID_K(8, NSLOT, ACC, pos_base, write, dst);                     \
+        else                                                                       \
+            DM_CENTROID_PASS(NSLOT, ACC, pos_base, write, dst);                    \
+    } while (0)
+
 template <bool BF16, int MSUB>
-__global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
+__global__ __launch_bounds__(kPanelWaves * 64, 2) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
                                                                  const uint8_t* __restrict__ Hp,
                                                                  const RowMeta* __restrict__ meta,
                                                                  float* __restrict__ logits,
@@ -497,7 +535,7 @@ __global__ __launch_bounds__(kPanelWaves * 64) void k_gemm_panel(const Plan P, c
         }
         if (lossy_tile) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-            DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
+            DM_CENTROIDS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
 #undef DM_ACC
         }
     };
@@ -749,8 +787,8 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
             }
             if (tile < P.tiles_lossy) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-                DM_CENTROID_PASS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
-                                 &my_st[ROWS + grp * P.ppg]);
+                DM_CENTROIDS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
+                             &my_st[ROWS + grp * P.ppg]);
 #undef DM_ACC
             }
         };
