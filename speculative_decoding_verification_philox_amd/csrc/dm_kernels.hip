@@ -1343,6 +1343,10 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     }
 }
 
+// KMAX bounds the heads the JS blocks hold in registers; the launch picks
+// the smallest of 5, 8 and kMaxK that covers K, so a kernel's register
+// budget (and with it how many waves a CU keeps in flight) follows K.
+template <int KMAX>
 __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const Plan P, const int32_t* __restrict__ draft, const float* __restrict__ q_hat,
     const float* __restrict__ logits, const RowStat* __restrict__ rowstat, const RowStat* __restrict__ centstat,
@@ -1355,10 +1359,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     (void)wave;
 
     if (blk < P.blk_js) {
-        if (K <= 8)
-            js_block<8>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
-        else
-            js_block<kMaxK>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
+        js_block<KMAX>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
         return;
     }
     blk -= P.blk_js;
@@ -2032,8 +2033,16 @@ hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat,
                         int32_t* accept_pos, uint32_t* data_status, uint8_t* dbg_flags, float* dbg_js_heads,
                         float* dbg_js_draft, hipStream_t st) {
     if (P.blk_js + P.blk_race > 0) {
-        hipLaunchKernelGGL(k_vocab, dim3(P.blk_js + P.blk_race), dim3(kVocabThreads), 0, st, P, draft, q_hat, logits,
-                           rowstat, centstat, jspart, race_best, filt);
+        const dim3 grid(P.blk_js + P.blk_race), block(kVocabThreads);
+        if (P.K <= 5)
+            hipLaunchKernelGGL(k_vocab<5>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
+                               race_best, filt);
+        else if (P.K <= 8)
+            hipLaunchKernelGGL(k_vocab<8>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
+                               race_best, filt);
+        else
+            hipLaunchKernelGGL(k_vocab<kMaxK>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat,
+                               jspart, race_best, filt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
