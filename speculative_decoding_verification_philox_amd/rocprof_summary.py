@@ -9,6 +9,13 @@
       --calib-kernel __amd_rocclr_copyBuffer --calib-bytes 1073741824 \
       --command "..." --json profiles/k_gemm_llama3_8b_head_traffic.json > profiles/Y.md
 
+  python -m speculative_decoding_verification_philox_amd.rocprof_summary counters \
+      RUN_counter_collection.csv --kernel k_gemm_tile --command "..." --title "..." > profiles/Z.md
+
+`counters` prints the mean per dispatch of every counter collected for one
+kernel, with the dispatch duration from the same records; MfmaFlopsBF16 is
+also turned into TFLOP/s over that duration.
+
 `traffic` turns the per-dispatch FETCH_SIZE / WRITE_SIZE counters (KiB) of a
 kernel into HBM bytes per launch.  Each counter is scaled by the factor that
 makes it read the known size of a plain copy kernel captured in the same run
@@ -132,6 +139,31 @@ def traffic(args) -> None:
           f"csrc/dm_common.hpp: `{kernel_source_hash(args.kernel)}`")
 
 
+def counters(args) -> None:
+    per: dict[str, list[float]] = {}
+    dur: dict[str, float] = {}
+    for r in csv.DictReader(open(args.csv)):
+        if args.kernel not in _short(r["Kernel_Name"]):
+            continue
+        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        dur[r["Dispatch_Id"]] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9
+    if not per:
+        raise SystemExit(f"no dispatch of {args.kernel} in {args.csv}")
+    t = statistics.mean(dur.values())
+    print(f"# {args.title}\n")
+    print(f"Command (from the repository root):\n\n```\n{args.command}\n```\n")
+    print(f"Dispatches of `{args.kernel}`: {len(dur)}; mean duration under counter collection {t * 1e6:.1f} us.\n")
+    print("| counter | mean per dispatch |")
+    print("|---|---|")
+    for name in sorted(per):
+        print(f"| {name} | {statistics.mean(per[name]):,.2f} |")
+    if "MfmaFlopsBF16" in per:
+        fl = statistics.mean(per["MfmaFlopsBF16"])
+        print(f"| bf16 matrix-core rate (MfmaFlopsBF16 / duration) | {fl / t / 1e12:,.1f} TFLOP/s |")
+    print(f"\nSource sha256 (first 16 hex digits) of the `{args.kernel}` section of csrc/dm_kernels.hip plus "
+          f"csrc/dm_common.hpp: `{kernel_source_hash(args.kernel)}`")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -139,6 +171,11 @@ def main(argv=None) -> None:
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -150,7 +187,7 @@ def main(argv=None) -> None:
     t.add_argument("--command", required=True)
     t.add_argument("--json", default=None)
     a = ap.parse_args(argv)
-    {"stats": stats, "traffic": traffic}[a.cmd](a)
+    {"stats": stats, "counters": counters, "traffic": traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":
