@@ -709,12 +709,18 @@ __global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const 
         if (refill) issue(st + NBUF - 1);
         if (has_tile) {
             const uint8_t* base = ring + (st % NBUF) * TS::STAGE + lane * 16;
+            const uint8_t* abase = base + (NW + wr * MSUB) * 1024;
             v4u w[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(base + (wc * G + g) * 1024);
+            // masked-row fragments one ahead: the next one's LDS read is in
+            // flight while the current one's products issue
+            v4u a_next = *(const v4u*)abase;
 #pragma unroll
             for (int m = 0; m < MSUB; ++m) {
-                const v4u afr = *(const v4u*)(base + (NW + wr * MSUB + m) * 1024);
+                const v4u afr = a_next;
+                if (m + 1 < MSUB) a_next = *(const v4u*)(abase + (m + 1) * 1024);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     if (BF16) {

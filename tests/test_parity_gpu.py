@@ -65,10 +65,12 @@ def test_bf16_ragged_vocab_mixed(K, layout):
     _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.25, range(1, 4), layout=layout)
 
 
-@pytest.mark.parametrize("B,gamma,K", [(1, 7, 5), (1, 3, 13), (2, 4, 3), (1, 0, 5)])
+@pytest.mark.parametrize("B,gamma,K", [(1, 7, 5), (1, 3, 13), (2, 4, 3), (1, 0, 5), (1, 7, 8), (2, 5, 5)])
 def test_bf16_one_tile_shapes(B, gamma, K, layout):
     """Shapes whose rows fit one tile (the B = 1 regime), |V| a panel multiple
-    and not, every rule."""
+    and not, every rule.  (1, 7, 8) and (2, 5, 5) fill 64-row tiles, where a
+    lane group holds two and three positions whose centroids are reduced
+    together; (1, 3, 13) takes the running centroid pass."""
     for V in (4096, 4099):
         w = wl.generate(1, B=B, gamma=gamma, d=1024, V=V, K=K, planted=0.8)
         modes = np.array([2, 0, 1][:B], np.uint8) if B < 3 else np.arange(B, dtype=np.uint8) % 3
