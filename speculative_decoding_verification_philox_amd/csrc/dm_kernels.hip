@@ -228,6 +228,7 @@ __device__ __forceinline__ float lossy_pos_inv_k(const Plan& P, int p) {
 constexpr int kPanelWaves = 4;
 constexpr int kPanelStrips = 4;
 constexpr int kPanelNK = 1;  // fragments per pipeline stage
+constexpr int kPanelDeepRing = 4;  // register ring of the few-wave variant
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 a .. 16 a + 15): swap
 // neighbours, then pairs, then mirror within each half row, then within the
@@ -418,8 +419,8 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
             DM_CENTROID_PASS(NSLOT, ACC, pos_base, write, dst);                    \
     } while (0)
 
-template <bool BF16, int MSUB>
-__global__ __launch_bounds__(kPanelWaves * 64, 2) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
+template <bool BF16, int MSUB, bool DEEP>
+__global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(const Plan P, const uint8_t* __restrict__ Wp,
                                                                  const uint8_t* __restrict__ Hp,
                                                                  const RowMeta* __restrict__ meta,
                                                                  float* __restrict__ logits,
@@ -446,44 +447,100 @@ __global__ __launch_bounds__(kPanelWaves * 64, 2) void k_gemm_panel(const Plan P
     if (active) {
         const uint8_t* wp = Wp + (size_t)panel * nkb * G * 1024 + lane * 16;
         const uint8_t* ap = Hp + (size_t)tile * nkb * MSUB * 1024 + lane * 16;
-        v4u wc[NK][G], ac[NK][MSUB], wn[NK][G], an[NK][MSUB];
-        auto load = [&](v4u (&w)[NK][G], v4u (&a)[NK][MSUB], int kb0) {
+        auto mma = [&](const v4u (&w)[G], const v4u (&a)[MSUB]) {
 #pragma unroll
-            for (int k = 0; k < NK; ++k) {
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    w[k][g] = __builtin_nontemporal_load((const v4u*)(wp + ((size_t)(kb0 + k) * G + g) * 1024));
+                for (int m = 0; m < MSUB; ++m) {
+                    if (BF16) {
+                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(v8bf, a[m]), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
+                    } else {
+                        const v4f a4 = __builtin_bit_cast(v4f, a[m]);
+                        const v4f b4 = __builtin_bit_cast(v4f, w[g]);
 #pragma unroll
-                for (int m = 0; m < MSUB; ++m) a[k][m] = *(const v4u*)(ap + ((size_t)(kb0 + k) * MSUB + m) * 1024);
-            }
-        };
-        load(wc, ac, 0);
-        for (int kb0 = 0; kb0 < nkb; kb0 += NK) {
-            if (kb0 + NK < nkb) load(wn, an, kb0 + NK);
-#pragma unroll
-            for (int k = 0; k < NK; ++k)
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int m = 0; m < MSUB; ++m) {
-                        if (BF16) {
-                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(v8bf, ac[k][m]), __builtin_bit_cast(v8bf, wc[k][g]), acc[g][m], 0,
-                                0, 0);
-                        } else {
-                            const v4f a = __builtin_bit_cast(v4f, ac[k][m]);
-                            const v4f b = __builtin_bit_cast(v4f, wc[k][g]);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[g][m], 0, 0, 0);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
                     }
+                }
+        };
+        if constexpr (DEEP) {
+            // Few waves on the whole GPU: each is bound by load latency, not
+            // by a share of the bandwidth, so it keeps D - 1 stages in flight
+            // while multiplying one (same stages, same order of products).
+            constexpr int D = kPanelDeepRing;
+            v4u wb[D][G], ab[D][MSUB];
+            auto load = [&](int slot, int kb) {
 #pragma unroll
-            for (int k = 0; k < NK; ++k) {
+                for (int g = 0; g < G; ++g)
+                    wb[slot][g] = __builtin_nontemporal_load((const v4u*)(wp + ((size_t)kb * G + g) * 1024));
 #pragma unroll
-                for (int g = 0; g < G; ++g) wc[k][g] = wn[k][g];
+                for (int m = 0; m < MSUB; ++m) ab[slot][m] = *(const v4u*)(ap + ((size_t)kb * MSUB + m) * 1024);
+            };
+            // prologue: stages 0 .. D - 2 (a row shorter than that re-reads its
+            // last fragment, never multiplied)
 #pragma unroll
-                for (int m = 0; m < MSUB; ++m) ac[k][m] = an[k][m];
+            for (int st = 0; st < D - 1; ++st) load(st, min(st, nkb - 1));
+            // steady state: every load a live stage and the same number of
+            // loads per step, so each wait is the fixed count issued after
+            int kb0 = 0;
+            for (; kb0 + 2 * D - 1 <= nkb; kb0 += D) {
+#pragma unroll
+                for (int k = 0; k < D; ++k) {
+                    load((k + D - 1) % D, kb0 + k + D - 1);  // the slot multiplied one step ago
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma(wb[k], ab[k]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // tail: at most 2 D - 2 stages, D - 1 of them already loaded
+#pragma unroll
+            for (int k = 0; k < 2 * D - 2; ++k) {
+                if (kb0 + k < nkb) {
+                    if (kb0 + k + D - 1 < nkb) load((k + D - 1) % D, kb0 + k + D - 1);
+                    mma(wb[k % D], ab[k % D]);
+                }
+            }
+        } else {
+            v4u wc[NK][G], ac[NK][MSUB], wn[NK][G], an[NK][MSUB];
+            auto load = [&](v4u (&w)[NK][G], v4u (&a)[NK][MSUB], int kb0) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        w[k][g] = __builtin_nontemporal_load((const v4u*)(wp + ((size_t)(kb0 + k) * G + g) * 1024));
+#pragma unroll
+                    for (int m = 0; m < MSUB; ++m) a[k][m] = *(const v4u*)(ap + ((size_t)(kb0 + k) * MSUB + m) * 1024);
+                }
+            };
+            load(wc, ac, 0);
+            for (int kb0 = 0; kb0 < nkb; kb0 += NK) {
+                if (kb0 + NK < nkb) load(wn, an, kb0 + NK);
+#pragma unroll
+                for (int k = 0; k < NK; ++k)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int m = 0; m < MSUB; ++m) {
+                            if (BF16) {
+                                acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(v8bf, ac[k][m]), __builtin_bit_cast(v8bf, wc[k][g]), acc[g][m], 0,
+                                    0, 0);
+                            } else {
+                                const v4f a = __builtin_bit_cast(v4f, ac[k][m]);
+                                const v4f b = __builtin_bit_cast(v4f, wc[k][g]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[g][m], 0, 0, 0);
+                            }
+                        }
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) wc[k][g] = wn[k][g];
+#pragma unroll
+                    for (int m = 0; m < MSUB; ++m) ac[k][m] = an[k][m];
+                }
             }
         }
     }
@@ -1951,17 +2008,30 @@ hipError_t launch_pack_w(const void* W, void* Wp, int V, int nkb, size_t n16, hi
     return hipGetLastError();
 }
 
+// The few-wave panel variant: fewer waves than the GPU has SIMDs (256 CUs x
+// 4), so no wave competes for bandwidth and latency bounds each one.
+static bool panel_deep(const Plan& P) { return (long long)P.n_panels * P.n_tiles < 1024; }
+
 template <bool BF16>
 static hipError_t launch_panel_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
                                  Stat* part, hipStream_t st) {
     dim3 grid((P.n_panels + kPanelWaves - 1) / kPanelWaves, P.n_tiles), block(kPanelWaves * 64);
     const uint8_t* w = (const uint8_t*)Wp;
     const uint8_t* a = (const uint8_t*)Hp;
+    if (panel_deep(P)) {
+        switch (P.msub) {
+            case 1: hipLaunchKernelGGL((k_gemm_panel<BF16, 1, true>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+            case 2: hipLaunchKernelGGL((k_gemm_panel<BF16, 2, true>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+            case 3: hipLaunchKernelGGL((k_gemm_panel<BF16, 3, true>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+            default: hipLaunchKernelGGL((k_gemm_panel<BF16, 4, true>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        }
+        return hipGetLastError();
+    }
     switch (P.msub) {
-        case 1: hipLaunchKernelGGL((k_gemm_panel<BF16, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 2: hipLaunchKernelGGL((k_gemm_panel<BF16, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 3: hipLaunchKernelGGL((k_gemm_panel<BF16, 3>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        default: hipLaunchKernelGGL((k_gemm_panel<BF16, 4>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 1: hipLaunchKernelGGL((k_gemm_panel<BF16, 1, false>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 2: hipLaunchKernelGGL((k_gemm_panel<BF16, 2, false>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 3: hipLaunchKernelGGL((k_gemm_panel<BF16, 3, false>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        default: hipLaunchKernelGGL((k_gemm_panel<BF16, 4, false>), grid, block, 0, st, P, w, a, meta, logits, part); break;
     }
     return hipGetLastError();
 }
