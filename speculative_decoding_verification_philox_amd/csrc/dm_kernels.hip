@@ -214,7 +214,9 @@ __device__ __forceinline__ float lossy_pos_inv_k(const Plan& P, int p) {
 // rows per 64-byte fragment; the tile's masked rows come from the packed Hm
 // (L2-resident, shared by every wave).  The next fragment's loads are in
 // flight while the current one feeds v_mfma_f32_16x16x32_bf16 (16x16x4 for
-// fp32).  No LDS and no barrier in the loop.
+// fp32).  No LDS and no barrier in the loop.  A grid of fewer waves than the
+// GPU has SIMDs (DEEP) keeps three stages in flight instead: with the
+// bandwidth not shared, each wave is bound by the latency of its loads.
 //
 // Epilogue, straight from the accumulators: lane 16 a + c holds column
 // 16 g + c of rows 16 m + 4 a + j.  Rows later passes need are stored; per
