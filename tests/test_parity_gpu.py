@@ -49,6 +49,19 @@ def test_tiny_config_each_mode(mode, layout):
     assert rep.decision_near_ties <= max(1, rep.decisions // 1000)
 
 
+def test_decision_statistics_over_twenty_seeds():
+    """Decisions over 20 Philox seeds at a multi-tile shape, every rule: about
+    9k decisions, so the near-tie allowance (oracle margin below 1e-4, at most
+    0.1% of decisions, each the only place a decision may differ) is measured
+    on enough of them to mean something."""
+    w = wl.generate(2, B=64, gamma=7, d=512, V=4099, K=5, planted=0.8)
+    modes = (np.arange(64) % 3).astype(np.uint8)
+    rep = _check(w.W, w.h, w.draft, w.q_hat, modes, w.K, 0.2, range(1, 21), layout=P.PANELS)
+    assert rep.decisions == 64 * 7 * 20
+    assert rep.decision_near_ties <= rep.decisions // 1000
+    assert rep.decision_mismatch_exempt <= rep.decision_near_ties
+
+
 def test_tiny_shapes_batched_mixed_modes(layout):
     """Config-0 shapes with 24 sequences of mixed rules: several GEMM tiles."""
     w = wl.generate(0, B=24)
