@@ -62,6 +62,41 @@ def test_decision_statistics_over_twenty_seeds():
     assert rep.decision_mismatch_exempt <= rep.decision_near_ties
 
 
+@pytest.mark.parametrize("where", ["first", "middle", "none"])
+def test_forced_rejection_positions(where, layout):
+    """Every rule with its outcome forced (K = 1, p = 0, so naive and JS accept
+    exactly the target argmax): the drafts before position r are the target
+    argmax (for lossless sequences with q(x) far below p(x)); draft r is the
+    target's least likely token (for lossless, with q one-hot on it).  Every
+    sequence then commits r drafts: r = 0, a middle position, or none
+    rejected (r = gamma, the bonus token)."""
+    G = 6
+    w = wl.generate(2, B=6, gamma=G, d=256, V=1000, K=1, planted=0.9)
+    modes = np.array([wl.NAIVE, wl.JS, wl.LOSSLESS] * 2, np.uint8)
+    # the target logits at K = 1, p = 0, from the oracle (undropped rows)
+    probe = P.oracle_run(w.W, w.h, w.draft, w.q_hat, np.full(6, wl.NAIVE, np.uint8), 1, 0.0, 1)
+    lg = probe["logits"][:, :, 0, :]  # [B, gamma + 1, V]
+    top = probe["head_argmax"][:, :, 0]
+    low = np.argmin(lg, axis=-1)
+    r = {"first": 0, "middle": G // 2, "none": G}[where]
+    draft = top[:, :G].astype(np.int32).copy()
+    q = np.full((6, G, 1000), 1e-7, np.float32)
+    if r < G:
+        draft[:, r] = low[:, r]
+        q[:, r, :] = 0.0
+        q[np.arange(6), r, low[:, r]] = 1.0
+    rep = P.Report()
+    for seed in (1, 2, 3):
+        o = P.oracle_run(w.W, w.h, draft, q, modes, 1, 0.0, seed)
+        np.testing.assert_array_equal(o["accept_len"], np.full(6, r))
+        ver = P.make_verifier(w.W, w.h, 1)
+        g = P.run_gpu(ver, P.Inputs(w.W, w.h, draft, q), modes, 1, 0.0, seed, layout=layout)
+        ver.close()
+        rep.add(P.compare(g, o, modes, 1))
+        np.testing.assert_array_equal(g["accept_len"], np.full(6, r))
+    print(rep, flush=True)
+
+
 def test_tiny_shapes_batched_mixed_modes(layout):
     """Config-0 shapes with 24 sequences of mixed rules: several GEMM tiles."""
     w = wl.generate(0, B=24)
