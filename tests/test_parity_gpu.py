@@ -97,6 +97,36 @@ def test_forced_rejection_positions(where, layout):
     print(rep, flush=True)
 
 
+def test_degenerate_head_ties_and_zero_residual(layout):
+    """W = 0, so every logit is 0: every head and centroid argmax is token 0
+    by the lowest-index tie rule, and p is uniform.  Sequences 0-2 draft
+    token 0 everywhere: naive and JS accept by the argmax and the majority,
+    lossless has q = p and never rejects (the bonus comes from p).
+    Sequences 3-5 draft token 5 with q(5) = 1 and q = 2/V elsewhere: every
+    rule rejects the first draft (lossless but for a 1/V chance), and the
+    lossless residual (p - q)+ is zero everywhere, so the emitted token is
+    drawn from p."""
+    G, V = 5, 1000
+    w = wl.generate(2, B=6, gamma=G, d=256, V=V, K=3, planted=0.0)
+    W0 = np.zeros_like(w.W)
+    modes = np.array([wl.NAIVE, wl.JS, wl.LOSSLESS] * 2, np.uint8)
+    draft = np.zeros((6, G), np.int32)
+    draft[3:] = 5
+    q = np.full((6, G, V), 1.0 / V, np.float32)
+    q[3:] = 2.0 / V
+    q[3:, :, 5] = 1.0
+    rep = _check(W0, w.h, draft, q, modes, 3, 0.2, range(1, 6), layout=layout)
+    assert rep.argmax_near_tie_mismatch == 0 and rep.decision_mismatch_exempt == 0
+    ver = P.make_verifier(W0, w.h, 3)
+    g = P.run_gpu(ver, P.Inputs(W0, w.h, draft, q), modes, 3, 0.2, 7, layout=layout)
+    ver.close()
+    lossy = modes != wl.LOSSLESS  # a lossless sequence has one undropped row; its other head slots hold -1
+    assert (g["head_argmax"][lossy] == 0).all() and (g["head_argmax"][~lossy][:, :, 0] == 0).all()
+    assert (g["head_argmax"][~lossy][:, :, 1:] == -1).all() and (g["centroid_argmax"] == 0).all()
+    np.testing.assert_array_equal(g["accept_len"][[0, 1, 2, 3, 4]], [G, G, G, 0, 0])
+    np.testing.assert_array_equal(g["out_token"][[0, 1, 3, 4]], [0, 0, 0, 0])
+
+
 def test_tiny_shapes_batched_mixed_modes(layout):
     """Config-0 shapes with 24 sequences of mixed rules: several GEMM tiles."""
     w = wl.generate(0, B=24)
