@@ -623,25 +623,28 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // k_gemm_tile: the LM head for many rows (the matrix-core-bound regime):
 // L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] (DropMatch Eq. (3)
 // with the shared head W).  One workgroup computes one group of four panels
-// (256 vocabulary columns) against a pair of row tiles (2 x 16 * MSUB rows).
+// (256 vocabulary columns) against kTileRowWaves row tiles of 16 * MSUB rows.
 //
-// Eight waves; wave w owns panel w % 4 of the group and tile w / 4 of the
-// pair, so each W fragment in LDS feeds two waves and each masked-row
-// fragment four.  Every wave also loads: a stage is one 64-byte slice of the
-// reduction index (16 W fragments and 2 x MSUB masked-row fragments of
-// 1 KiB), copied from global memory straight into a kTileNBUF-deep LDS ring
-// (direct global-to-LDS loads, 16 bytes per lane, one instruction per
-// fragment, the fragments dealt round-robin to the waves).  Per stage a wave
-// refills the slot freed at the last barrier, multiplies the current slot
-// (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4 for fp32), waits until its
-// own loads of the next stage have landed, and meets the others at one
-// barrier.  The barrier is a bare s_barrier: the workgroup fence of an
-// ordinary barrier would also wait for the loads of the later stages still
-// in flight, which empties the ring every stage.
+// Four waves per row tile; wave w owns panel w % 4 of the group and tile
+// w / 4, so each W fragment in LDS feeds kTileRowWaves waves and each
+// masked-row fragment four.  Every wave also loads: a stage is one 64-byte
+// slice of the reduction index (16 W fragments and kTileRowWaves x MSUB
+// masked-row fragments of 1 KiB), copied from global memory straight into a
+// kTileNBUF-deep LDS ring (direct global-to-LDS loads, 16 bytes per lane,
+// one instruction per fragment, the fragments dealt round-robin to the
+// waves).  Per stage a wave refills the slot freed at the last barrier,
+// multiplies the current slot (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4
+// for fp32), waits until its own loads of the next stage have landed, and
+// meets the others at one barrier.  The barrier is a bare s_barrier: the
+// workgroup fence of an ordinary barrier would also wait for the loads of
+// the later stages still in flight, which empties the ring every stage.
 //
-// Per multiply-add this fetches a third fewer operand bytes than a 256 x
-// 160 tile; the path from L2 into the CUs is what bounds the loop.  Blocks
-// are mapped so that the tile pairs sharing a panel group run together on
+// One row tile per workgroup: a 3-deep ring of 26 KiB stages lets two
+// workgroups share a CU (one wave each per SIMD, 78 KiB of LDS each), and
+// each meets only its own barrier, so one feeds the matrix cores while the
+// other waits.  That outweighs fetching each W fragment into LDS twice per
+// CU (a workgroup of two row tiles shares it but owns the CU's LDS alone).
+// Blocks are mapped so that the tiles sharing a panel group run together on
 // one XCD (workgroups go to the eight XCDs in turn), where the group's W is
 // read from HBM once and then from that XCD's L2.
 //
@@ -650,10 +653,10 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // part[target][panel group]; stored rows written.
 // =====================================================================
 constexpr int kTileColWaves = 4;  // 64-column panels per workgroup
-constexpr int kTileRowWaves = 2;  // row tiles per workgroup
+constexpr int kTileRowWaves = 1;  // row tiles per workgroup
 constexpr int kTileWaves = kTileColWaves * kTileRowWaves;
 constexpr int kTileThreads = kTileWaves * 64;
-constexpr int kTileNBUF = 4;  // stages in the LDS ring
+constexpr int kTileNBUF = 3;  // stages in the LDS ring
 
 template <int MSUB>
 struct TileShape {
@@ -686,7 +689,7 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 template <bool BF16, int MSUB>
-__global__ __launch_bounds__(kTileThreads) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
+__global__ __launch_bounds__(kTileThreads, 2) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
                                                             const uint8_t* __restrict__ Hp,
                                                             const RowMeta* __restrict__ meta,
                                                             float* __restrict__ logits,

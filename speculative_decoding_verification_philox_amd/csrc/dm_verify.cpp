@@ -141,11 +141,11 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         }
     }
     // Panel-ordered W with more rows than one small tile holds: the
-    // matrix-core kernel, tiles of 4..10 sub-tiles taken two at a time.  A
-    // workgroup computes 2 MT x 256 outputs from (2 MT + 256) operand rows
-    // per fragment, so the cost of a choice is its tile pairs times
-    // (2 MT + 256), the operand rows fetched per fragment over the whole
-    // grid; the cheapest wins, ties going to the larger tile.
+    // matrix-core kernel, tiles of 4..10 sub-tiles, one per workgroup.  A
+    // workgroup computes MT x 256 outputs from (MT + 256) operand rows per
+    // fragment, so the cost of a choice is its tiles times (MT + 256), the
+    // operand rows fetched per fragment over the whole grid; the cheapest
+    // wins, ties going to the larger tile.
     P.tile_kernel = 0;
     if (w_packed && best_tiles > 1) {
         P.tile_kernel = 1;
@@ -157,7 +157,7 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
             const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
             const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
             const double mt = 16.0 * ms;
-            const double cost = (double)((tl + tn + 1) / 2) * (2.0 * mt + 256.0);
+            const double cost = (double)(tl + tn) * (mt + 256.0);
             if (best_ms == 0 || cost <= best_cost) {
                 best_ms = ms;
                 best_cost = cost;
