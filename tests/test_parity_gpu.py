@@ -305,3 +305,45 @@ def test_dropout_extremes(p_drop, layout):
     w = wl.generate(2, B=5, gamma=4, d=256, V=2048, K=5, planted=0.8)
     modes = np.array([2, 1, 0, 2, 1], np.uint8)
     _check(w.W, w.h, w.draft, w.q_hat, modes, 5, p_drop, [4, 2**33 + 9], layout=layout)
+
+
+# ------------------------------------------ the matrix-core tile kernel
+def _tile_choice(n_pos, K):
+    """Sub-tiles per tile and tile count the library's planner takes for
+    panel-order W when every sequence has a lossy rule (n_pos positions of K
+    head rows): 64-row tiles first; past one of those, tiles of 4..10
+    sub-tiles of 16 rows, the smallest tiles x (16 * sub-tiles + 256), ties
+    to the larger tile.  Used only to choose and label the cases below."""
+    def tiles(ms):
+        return -(-n_pos // (4 * ((4 * ms) // K)))
+    small = min(tiles(ms) for ms in range(1, 5) if 4 * ms >= K)
+    if small <= 1:
+        return None
+    best = min(range(4, 11), key=lambda ms: (tiles(ms) * (16 * ms + 256), -ms))
+    return best, tiles(best)
+
+
+# (B, gamma, K, |V|): sub-tile counts 5..10 at one to five tiles.  |V| = 1000
+# leaves four panel groups (the last panel 40 columns wide), so four of the
+# eight XCD slots idle; |V| = 2100 leaves a ninth group holding one
+# 52-column panel.
+TILE_CASES = [(1, 4, 9, 1000), (1, 12, 11, 2100), (2, 8, 14, 1000), (3, 10, 15, 2100), (5, 4, 11, 1000),
+              (7, 6, 10, 2100), (5, 4, 13, 2100)]
+
+
+def test_tile_cases_cover_every_sub_tile_count():
+    got = {_tile_choice(B * (G + 1), K) for B, G, K, _ in TILE_CASES}
+    assert {c[0] for c in got} == set(range(5, 11)) and {c[1] for c in got} == {1, 2, 3, 4, 5}
+
+
+@pytest.mark.parametrize("B,gamma,K,V", TILE_CASES, ids=[f"B{b}g{g}K{k}V{v}" for b, g, k, v in TILE_CASES])
+def test_tile_kernel_every_sub_tile_count(B, gamma, K, V):
+    """Panel-order W at row counts that take the tile kernel with each of its
+    sub-tile counts, bf16, every sequence on the JS rule (the planned shape)
+    and then on mixed rules (lossless rows in tiles of their own)."""
+    print(f"  tile plan (sub-tiles, tiles) = {_tile_choice(B * (gamma + 1), K)}", flush=True)
+    w = wl.generate(1, B=B, gamma=gamma, d=320, V=V, K=K, planted=0.8)
+    _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, range(1, 3), layout=P.PANELS)
+    if B > 1:
+        modes = np.arange(B, dtype=np.uint8) % 3
+        _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.3, [7], layout=P.PANELS)
