@@ -308,15 +308,18 @@ def test_dropout_extremes(p_drop, layout):
 
 
 # ------------------------------------------ the matrix-core tile kernel
-def _tile_choice(n_pos, K):
+def _tile_choice(n_pos, K, n_lossless=0):
     """Sub-tiles per tile and tile count the library's planner takes for
-    panel-order W when every sequence has a lossy rule (n_pos positions of K
-    head rows): 64-row tiles first; past one of those, tiles of 4..10
-    sub-tiles of 16 rows, the smallest tiles x (16 * sub-tiles + 256), ties
-    to the larger tile.  Used only to choose and label the cases below."""
+    panel-order W with n_pos lossy positions (K head rows each, four lane
+    groups of (4 * sub-tiles) // K positions per tile) and n_lossless
+    lossless positions (one row each, in tiles of their own): 64-row tiles
+    first; past one of those, tiles of 4..10 sub-tiles of 16 rows, the
+    smallest tiles x (16 * sub-tiles + 256), ties to the larger tile.  Used
+    only to choose and label the cases below."""
     def tiles(ms):
-        return -(-n_pos // (4 * ((4 * ms) // K)))
-    small = min(tiles(ms) for ms in range(1, 5) if 4 * ms >= K)
+        tl = -(-n_pos // (4 * ((4 * ms) // K))) if n_pos else 0
+        return tl + (-(-n_lossless // (16 * ms)) if n_lossless else 0)
+    small = min(tiles(ms) for ms in range(1, 5) if 4 * ms >= K or not n_pos)
     if small <= 1:
         return None
     best = min(range(4, 11), key=lambda ms: (tiles(ms) * (16 * ms + 256), -ms))
@@ -334,6 +337,9 @@ TILE_CASES = [(1, 4, 9, 1000), (1, 12, 11, 2100), (2, 8, 14, 1000), (3, 10, 15, 
 def test_tile_cases_cover_every_sub_tile_count():
     got = {_tile_choice(B * (G + 1), K) for B, G, K, _ in TILE_CASES}
     assert {c[0] for c in got} == set(range(5, 11)) and {c[1] for c in got} == {1, 2, 3, 4, 5}
+    # four sub-tiles: only when lossy and lossless rows each fill one 64-row tile
+    assert _tile_choice(8, 5, n_lossless=8) == (4, 2)
+    assert all(_tile_choice(n, K)[0] > 4 for n in range(1, 400) for K in range(1, 17) if _tile_choice(n, K))
 
 
 @pytest.mark.parametrize("B,gamma,K,V", TILE_CASES, ids=[f"B{b}g{g}K{k}V{v}" for b, g, k, v in TILE_CASES])
@@ -347,3 +353,13 @@ def test_tile_kernel_every_sub_tile_count(B, gamma, K, V):
     if B > 1:
         modes = np.arange(B, dtype=np.uint8) % 3
         _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.3, [7], layout=P.PANELS)
+
+
+def test_tile_kernel_four_sub_tiles_mixed_rules():
+    """One JS and one lossless sequence of eight positions at K = 5: each
+    rule's rows fill one 64-row tile, so the tile kernel runs with four
+    sub-tiles and two tiles."""
+    assert _tile_choice(8, 5, n_lossless=8) == (4, 2)
+    w = wl.generate(1, B=2, gamma=7, d=320, V=1000, K=5, planted=0.8)
+    modes = np.array([wl.JS, wl.LOSSLESS], np.uint8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, 5, 0.2, range(1, 4), layout=P.PANELS)
