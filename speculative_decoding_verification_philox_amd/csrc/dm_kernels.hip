@@ -6,9 +6,9 @@
 //   k_gemm_panel  LM-head GEMM over panel-ordered W: one wave streams one
 //                 panel of 64 vocabulary rows straight into MFMA operands,
 //                 with a softmax-statistics epilogue per row and per centroid
-//   k_gemm_tile   the same for many rows: tiles of up to 160 rows, four
-//                 panels per workgroup, loader waves filling an LDS ring for
-//                 compute waves, XCD-aware order
+//   k_gemm_tile   the same for many rows: one tile of up to 160 rows x four
+//                 panels per workgroup of four waves that all fill an LDS
+//                 ring and multiply, two workgroups per CU, XCD-aware order
 //   k_gemm_skinny LM-head GEMM over row-major W (all rows of a tile in one
 //                 workgroup; W streamed from HBM straight into MFMA operands),
 //                 same epilogue
@@ -18,7 +18,7 @@
 //   k_vocab       Jensen-Shannon terms and the residual race over the
 //                 vocabulary
 //   k_finish      acceptance rule per drafted position, first-rejection
-//                 scan and the emitted token, one wave per sequence
+//                 scan and the emitted token, one workgroup per sequence
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
