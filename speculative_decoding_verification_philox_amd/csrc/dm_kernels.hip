@@ -122,11 +122,15 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
     const size_t n16 = (size_t)P.R_phys * P.nkb * 4;
     if (q >= n16) return;
     const int lane = (int)(q & 63);
-    const size_t frag = q >> 6;  // (tile * nkb + kb) * msub + m
-    const int m = (int)(frag % (size_t)P.msub);
-    const size_t tk = frag / (size_t)P.msub;
-    const int kb = (int)(tk % (size_t)P.nkb);
-    const int tile = (int)(tk / (size_t)P.nkb);
+    // (tile * nkb + kb) * msub + m: at most R_phys * nkb / 16 fragments, far
+    // below 2^32, so the index splits in 32-bit arithmetic
+    const uint32_t frag = (uint32_t)(q >> 6);
+    const uint32_t msub = (uint32_t)P.msub, nkb = (uint32_t)P.nkb;
+    const uint32_t tk = frag / msub;
+    const int m = (int)(frag - tk * msub);
+    const uint32_t tile_u = tk / nkb;
+    const int kb = (int)(tk - tile_u * nkb);
+    const int tile = (int)tile_u;
     const int r = 16 * m + (lane & 15);
     const int rho = tile * P.MT + r;
     const int o = kb * 64 + (lane >> 4) * 16;  // byte offset within the row
