@@ -627,27 +627,28 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // k_gemm_tile: the LM head for many rows (the matrix-core-bound regime):
 // L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] (DropMatch Eq. (3)
 // with the shared head W).  One workgroup computes one group of four panels
-// (256 vocabulary columns) against kTileRowWaves row tiles of 16 * MSUB rows.
+// (256 vocabulary columns) against WR row tiles of 16 * MSUB rows.
 //
 // Four waves per row tile; wave w owns panel w % 4 of the group and tile
-// w / 4, so each W fragment in LDS feeds kTileRowWaves waves and each
-// masked-row fragment four.  Every wave also loads: a stage is one 64-byte
-// slice of the reduction index (16 W fragments and kTileRowWaves x MSUB
-// masked-row fragments of 1 KiB), copied from global memory straight into a
-// kTileNBUF-deep LDS ring (direct global-to-LDS loads, 16 bytes per lane,
-// one instruction per fragment, the fragments dealt round-robin to the
-// waves).  Per stage a wave refills the slot freed at the last barrier,
-// multiplies the current slot (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4
-// for fp32), waits until its own loads of the next stage have landed, and
-// meets the others at one barrier.  The barrier is a bare s_barrier: the
-// workgroup fence of an ordinary barrier would also wait for the loads of
-// the later stages still in flight, which empties the ring every stage.
+// w / 4, so each W fragment in LDS feeds WR waves and each masked-row
+// fragment four.  Every wave also loads: a stage is one 64-byte slice of the
+// reduction index (16 W fragments and WR x MSUB masked-row fragments of
+// 1 KiB), copied from global memory straight into a kTileNBUF-deep LDS ring
+// (direct global-to-LDS loads, 16 bytes per lane, one instruction per
+// fragment, the fragments dealt round-robin to the waves).  Per stage a wave
+// refills the slot freed at the last barrier, multiplies the current slot
+// (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4 for fp32), waits until its own
+// loads of the next stage have landed, and meets the others at one barrier.
+// The barrier is a bare s_barrier: the workgroup fence of an ordinary
+// barrier would also wait for the loads of the later stages still in
+// flight, which empties the ring every stage.
 //
-// One row tile per workgroup: a 3-deep ring of 26 KiB stages lets two
-// workgroups share a CU (one wave each per SIMD, 78 KiB of LDS each), and
-// each meets only its own barrier, so one feeds the matrix cores while the
-// other waits.  That outweighs fetching each W fragment into LDS twice per
-// CU (a workgroup of two row tiles shares it but owns the CU's LDS alone).
+// A 3-deep ring of stages of at most 26 KiB lets two workgroups share a CU
+// (78 KiB of LDS each), and each meets only its own barrier, so one feeds
+// the matrix cores while the other waits.  WR = 1 (tiles of up to 10
+// sub-tiles, one wave of each workgroup per SIMD) is the usual shape; WR = 2
+// (two tiles of 4 or 5 sub-tiles, eight waves, two of each workgroup per
+// SIMD) serves plans whose rows pack with less padding into smaller tiles.
 // Blocks are mapped so that the tiles sharing a panel group run together on
 // one XCD (workgroups go to the eight XCDs in turn), where the group's W is
 // read from HBM once and then from that XCD's L2.
@@ -657,17 +658,16 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // part[target][panel group]; stored rows written.
 // =====================================================================
 constexpr int kTileColWaves = 4;  // 64-column panels per workgroup
-constexpr int kTileRowWaves = 1;  // row tiles per workgroup
-constexpr int kTileWaves = kTileColWaves * kTileRowWaves;
-constexpr int kTileThreads = kTileWaves * 64;
-constexpr int kTileNBUF = 3;  // stages in the LDS ring
+constexpr int kTileNBUF = 3;      // stages in the LDS ring
 
-template <int MSUB>
+// WR row tiles of MSUB sub-tiles per workgroup
+template <int MSUB, int WR>
 struct TileShape {
-    static constexpr int NW = kTileColWaves * 4;     // W fragments per stage
-    static constexpr int NA = kTileRowWaves * MSUB;  // masked-row fragments per stage
+    static constexpr int WAVES = kTileColWaves * WR;
+    static constexpr int NW = kTileColWaves * 4;  // W fragments per stage
+    static constexpr int NA = WR * MSUB;          // masked-row fragments per stage
     static constexpr int NF = NW + NA;
-    static constexpr int NJ = (NF + kTileWaves - 1) / kTileWaves;  // most fragments one wave loads per stage
+    static constexpr int NJ = (NF + WAVES - 1) / WAVES;  // most fragments one wave loads per stage
     static constexpr int STAGE = NF * 1024;
     static constexpr int LDS = kTileNBUF * STAGE;
 };
@@ -692,14 +692,14 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <bool BF16, int MSUB>
-__global__ __launch_bounds__(kTileThreads, 2) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
+template <bool BF16, int MSUB, int WR>
+__global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
                                                             const uint8_t* __restrict__ Hp,
                                                             const RowMeta* __restrict__ meta,
                                                             float* __restrict__ logits,
                                                             Stat* __restrict__ part) {
-    using TS = TileShape<MSUB>;
-    constexpr int ROWS = 16 * MSUB, G = 4, WC = kTileColWaves, WR = kTileRowWaves, NBUF = kTileNBUF;
+    using TS = TileShape<MSUB, WR>;
+    constexpr int ROWS = 16 * MSUB, G = 4, WC = kTileColWaves, NBUF = kTileNBUF, kTileWaves = TS::WAVES;
     constexpr int NW = TS::NW, NF = TS::NF, NJ = TS::NJ;
     constexpr size_t ST_BYTES = (size_t)WR * WC * 2 * ROWS * sizeof(Stat);
     static_assert(ST_BYTES + WR * ROWS * sizeof(RowMeta) <= (size_t)TS::LDS, "epilogue fits in the ring");
@@ -2063,20 +2063,29 @@ static hipError_t launch_skinny_t(const Plan& P, const void* W, const void* Hm, 
 template <bool BF16>
 static hipError_t launch_tile_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
                                 Stat* part, hipStream_t st) {
+    const int WR = P.tile_kernel == 2 ? 2 : 1;  // row tiles per workgroup
     const int n_groups = (P.n_panels + 3) / 4;
     const int per_xcd = (n_groups + 7) / 8;
-    const int n_pairs = (P.n_tiles + kTileRowWaves - 1) / kTileRowWaves;
-    dim3 grid(8 * per_xcd * n_pairs), block(kTileThreads);
+    const int n_pairs = (P.n_tiles + WR - 1) / WR;
+    dim3 grid(8 * per_xcd * n_pairs), block(kTileColWaves * 64 * WR);
     const uint8_t* w = (const uint8_t*)Wp;
     const uint8_t* a = (const uint8_t*)Hp;
+    if (WR == 2) {
+        switch (P.msub) {
+            case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+            case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (P.msub) {
-        case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 6: hipLaunchKernelGGL((k_gemm_tile<BF16, 6>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 6: hipLaunchKernelGGL((k_gemm_tile<BF16, 6, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

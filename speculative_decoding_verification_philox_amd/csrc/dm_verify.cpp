@@ -141,29 +141,41 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         }
     }
     // Panel-ordered W with more rows than one small tile holds: the
-    // matrix-core kernel, tiles of 4..10 sub-tiles, one per workgroup.  A
-    // workgroup computes MT x 256 outputs from (MT + 256) operand rows per
-    // fragment, so the cost of a choice is its tiles times (MT + 256), the
-    // operand rows fetched per fragment over the whole grid; the cheapest
-    // wins, ties going to the larger tile.
+    // matrix-core kernel.  A workgroup of WR row tiles computes WR*MT x 256
+    // outputs from (WR*MT + 256) operand rows per fragment, so for each WR
+    // the cost of a sub-tile count is its workgroups times that, the operand
+    // rows fetched per fragment over the whole grid; the cheapest wins, ties
+    // going to the larger tile.  One tile per workgroup (4..10 sub-tiles,
+    // four waves) is the default; two tiles of 4..5 sub-tiles (eight waves,
+    // four per SIMD) run as fast per computed row and are taken when their
+    // smaller tiles cut the computed rows (padding included) by at least 5%.
     P.tile_kernel = 0;
     if (w_packed && best_tiles > 1) {
-        P.tile_kernel = 1;
-        best_ms = 0;
-        double best_cost = 0.0;
-        for (int ms = 4; ms <= 10; ++ms) {
+        auto tiles_for = [&](int ms) {
             const int S = 4 * ms;
-            const int ppg = S / K;
+            const int ppg = S / K;  // >= 1: S >= 16 >= K
             const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
             const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
-            const double mt = 16.0 * ms;
-            const double cost = (double)(tl + tn) * (mt + 256.0);
-            if (best_ms == 0 || cost <= best_cost) {
-                best_ms = ms;
-                best_cost = cost;
-                best_tiles = tl + tn;
+            return tl + tn;
+        };
+        int ms_wr[3] = {0, 0, 0}, tiles_wr[3] = {0, 0, 0};
+        for (int wr = 1; wr <= 2; ++wr) {
+            double best_cost = 0.0;
+            for (int ms = 4; ms <= (wr == 1 ? 10 : 5); ++ms) {
+                const int t = tiles_for(ms);
+                const double cost = (double)((t + wr - 1) / wr) * (wr * 16.0 * ms + 256.0);
+                if (ms_wr[wr] == 0 || cost <= best_cost) {
+                    ms_wr[wr] = ms;
+                    tiles_wr[wr] = t;
+                    best_cost = cost;
+                }
             }
         }
+        const long long rows1 = (long long)tiles_wr[1] * 16 * ms_wr[1];
+        const long long rows2 = (long long)tiles_wr[2] * 16 * ms_wr[2];
+        P.tile_kernel = rows2 * 100 <= rows1 * 95 ? 2 : 1;
+        best_ms = ms_wr[P.tile_kernel];
+        best_tiles = tiles_wr[P.tile_kernel];
     }
     P.msub = best_ms;
     P.MT = 16 * best_ms;
