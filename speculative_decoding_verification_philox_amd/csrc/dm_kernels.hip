@@ -6,9 +6,10 @@
 //   k_gemm_panel  LM-head GEMM over panel-ordered W: one wave streams one
 //                 panel of 64 vocabulary rows straight into MFMA operands,
 //                 with a softmax-statistics epilogue per row and per centroid
-//   k_gemm_tile   the same for many rows: one tile of up to 160 rows x four
-//                 panels per workgroup of four waves that all fill an LDS
-//                 ring and multiply, two workgroups per CU, XCD-aware order
+//   k_gemm_tile   the same for many rows: four panels x one tile of up to
+//                 160 rows (four waves) or two of up to 80 (eight waves) per
+//                 workgroup, all waves filling an LDS ring and multiplying,
+//                 two workgroups per CU, XCD-aware order
 //   k_gemm_skinny LM-head GEMM over row-major W (all rows of a tile in one
 //                 workgroup; W streamed from HBM straight into MFMA operands),
 //                 same epilogue
