@@ -226,8 +226,10 @@ __device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
-        uint32_t hi0 = __umulhi(m0, c.x), lo0 = m0 * c.x;
-        uint32_t hi1 = __umulhi(m1, c.z), lo1 = m1 * c.z;
+        // one 32 x 32 -> 64-bit product gives both halves (v_mad_u64_u32)
+        const uint64_t p0 = (uint64_t)m0 * c.x, p1 = (uint64_t)m1 * c.z;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
