@@ -7,10 +7,13 @@ the scan and the emitted token.  Prints one JSON line on stdout.
 
   python bench.py [--steps K] [--warmup W] [--config C]
 
-The default workload is the Llama-3-8B-shaped head (B = 1, gamma = 7,
-d = 4096, |V| = 128256, K = 5, p_drop = 0.2, JS + majority).  --config picks
-another workload for inspection (0-4: chains; 5: naive matching on a 60-node
-token tree at the 70B head).
+The default workload is the batched Llama-3.1-70B-shaped head (B = 32,
+gamma = 7, d = 8192, |V| = 128256, K = 5, p_drop = 0.25, JS + majority:
+1280 LM-head rows, the largest K = 5 workload on one GPU, where the GEMM is
+bound by the matrix cores).  --config picks another workload for
+inspection (0: tiny; 1, 2: the 8B and 70B heads at B = 1, bound by HBM;
+4: wide vocabulary, mixed rules; 5: naive matching on a 60-node token tree
+at the 70B head).
 """
 from __future__ import annotations
 
@@ -103,27 +106,64 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_info():
+    """(CPU model string, nproc, CPUs this process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = nproc
+    return model, nproc, avail
+
+
 def cpu_baseline(w, seed, budget_s):
-    """The oracle as it stands, timed on a bounded sample of the same workload:
-    whole sequences (every position of a sequence, all its heads) taken in
-    batch order, repeated until about `budget_s` seconds of CPU work."""
+    """The oracle as it stands, timed on bounded samples of the same workload.
+
+    All threads (at most 16, the host share of one GPU): whole sequences
+    (every position of a sequence, all its heads, full vocabulary) in batch
+    order until about `budget_s` seconds.  One thread: single positions of
+    the same sequences (the sequence cut to its first position through the
+    ragged-batch inputs: all heads, full vocabulary) until about a third of
+    that."""
     import numpy as np
 
     import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    model, nproc, avail = cpu_info()
+    threads = max(1, min(16, avail))
     B = w.cfg.B
-    done_pos, elapsed, calls = 0, 0.0, 0
-    while elapsed < budget_s:
-        t0 = time.perf_counter()
-        oracle.run(w.W, w.h, w.draft, w.q_hat, w.modes, w.K, w.p_drop, seed, seqs=np.array([calls % B], np.int32),
-                   n_threads=threads, tree_parent=w.tree_parent)
-        elapsed += time.perf_counter() - t0
-        done_pos += w.cfg.gamma + 1
-        calls += 1
-    return {"value": round(done_pos / elapsed, 3), "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} oracle call(s) of one sequence each ({w.cfg.gamma + 1} positions, all heads, "
-                      f"full vocabulary) of the same workload, fp64, {elapsed:.1f} s"}
+
+    def sample(n_threads, one_position, budget):
+        done, elapsed, calls = 0, 0.0, 0
+        while elapsed < budget or calls == 0:
+            b = calls % B
+            kw = {}
+            if one_position:
+                kw["seq_gamma"] = np.zeros(B, np.int32)
+            t0 = time.perf_counter()
+            oracle.run(w.W, w.h, w.draft, w.q_hat, w.modes, w.K, w.p_drop, seed, seqs=np.array([b], np.int32),
+                       n_threads=n_threads, tree_parent=w.tree_parent, **kw)
+            elapsed += time.perf_counter() - t0
+            done += 1 if one_position else w.cfg.gamma + 1
+            calls += 1
+        return done / elapsed, calls, elapsed
+
+    rate, calls, el = sample(threads, False, budget_s)
+    rate1, calls1, el1 = sample(1, True, budget_s / 3.0)
+    return {"value": round(rate, 3), "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{threads} threads: {calls} oracle call(s) of one whole sequence each "
+                      f"({w.cfg.gamma + 1} positions, all heads, full vocabulary) of the same workload, fp64, "
+                      f"{el:.1f} s; 1 thread: {calls1} call(s) of one position each, {el1:.1f} s",
+            "single_thread_value": round(rate1, 4), "nproc": nproc, "cpus_available": avail, "cpu_model": model}
 
 
 def copy_probe(nbytes: int, dev) -> None:
@@ -146,7 +186,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--p-drop", type=float, default=None)
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="sampling temperature of the target (every rule)")
@@ -271,7 +311,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores ...")
         cpu = cpu_baseline(w, seed, args.cpu_seconds)
-        log(f"[bench] oracle {cpu['value']:.3f} positions/s on {cpu['cores']} threads")
+        log(f"[bench] oracle {cpu['value']:.3f} positions/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread_value']:.4f} on one")
 
     modes_desc = {"js": "JS+majority", "naive": "naive", "lossless": "lossless",
                   "half_lossless_naive": "half lossless / half naive",

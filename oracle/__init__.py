@@ -55,16 +55,51 @@ class _Result(ctypes.Structure):
     ]
 
 
-def build() -> str:
-    """Compile the oracle with gcc (plain C, IEEE fp64, OpenMP over vocab rows)."""
-    tmp = _LIB + ".tmp"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"],
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain C, IEEE fp64, OpenMP over vocab rows).
+    `src` / `out` default to the oracle itself; the tests also build edited
+    copies (a planted mistake) to show that a pin catches it."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, src, "-lm"],
                    check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Open a built oracle library and declare its entry points."""
+    L = ctypes.CDLL(path)
+    L.dmo_philox4x32_10.argtypes = [_c_u32p, _c_u32p, _c_u32p]
+    L.dmo_philox4x32_10.restype = None
+    L.dmo_threshold.argtypes = [ctypes.c_float]
+    L.dmo_threshold.restype = ctypes.c_uint32
+    L.dmo_accept_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+    L.dmo_accept_uniform.restype = ctypes.c_double
+    L.dmo_race_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
+    L.dmo_race_uniform.restype = ctypes.c_double
+    L.dmo_row_stats.argtypes = [_c_f64p, ctypes.c_int, _c_f64p, _c_f64p, _c_i32p, _c_f64p]
+    L.dmo_row_stats.restype = None
+    L.dmo_js.argtypes = [_c_f64p, _c_f64p, ctypes.c_int]
+    L.dmo_js.restype = ctypes.c_double
+    L.dmo_race.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, _c_f64p]
+    L.dmo_race.restype = ctypes.c_int32
+    L.dmo_rule_naive.argtypes = [_c_i32p, ctypes.c_int, ctypes.c_int32]
+    L.dmo_rule_naive.restype = ctypes.c_int
+    L.dmo_rule_js.argtypes = [ctypes.c_double, ctypes.c_double, _c_i32p, ctypes.c_int, ctypes.c_int32]
+    L.dmo_rule_js.restype = ctypes.c_int
+    L.dmo_rule_lossless.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    L.dmo_rule_lossless.restype = ctypes.c_int
+    L.dmo_processed.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f64p, _c_f64p,
+                                _c_f64p]
+    L.dmo_processed.restype = ctypes.c_int
+    L.dmo_tree_walk.argtypes = [_c_i32p, _c_u8p, ctypes.c_int, _c_i32p]
+    L.dmo_tree_walk.restype = ctypes.c_int
+    L.dmo_run.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Result)]
+    L.dmo_run.restype = ctypes.c_int
+    return L
 
 
 def lib() -> ctypes.CDLL:
@@ -72,35 +107,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
-        L = ctypes.CDLL(_LIB)
-        L.dmo_philox4x32_10.argtypes = [_c_u32p, _c_u32p, _c_u32p]
-        L.dmo_philox4x32_10.restype = None
-        L.dmo_threshold.argtypes = [ctypes.c_float]
-        L.dmo_threshold.restype = ctypes.c_uint32
-        L.dmo_accept_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
-        L.dmo_accept_uniform.restype = ctypes.c_double
-        L.dmo_race_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
-        L.dmo_race_uniform.restype = ctypes.c_double
-        L.dmo_row_stats.argtypes = [_c_f64p, ctypes.c_int, _c_f64p, _c_f64p, _c_i32p, _c_f64p]
-        L.dmo_row_stats.restype = None
-        L.dmo_js.argtypes = [_c_f64p, _c_f64p, ctypes.c_int]
-        L.dmo_js.restype = ctypes.c_double
-        L.dmo_race.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, _c_f64p]
-        L.dmo_race.restype = ctypes.c_int32
-        L.dmo_rule_naive.argtypes = [_c_i32p, ctypes.c_int, ctypes.c_int32]
-        L.dmo_rule_naive.restype = ctypes.c_int
-        L.dmo_rule_js.argtypes = [ctypes.c_double, ctypes.c_double, _c_i32p, ctypes.c_int, ctypes.c_int32]
-        L.dmo_rule_js.restype = ctypes.c_int
-        L.dmo_rule_lossless.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
-        L.dmo_rule_lossless.restype = ctypes.c_int
-        L.dmo_processed.argtypes = [_c_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f64p, _c_f64p,
-                                    _c_f64p]
-        L.dmo_processed.restype = ctypes.c_int
-        L.dmo_tree_walk.argtypes = [_c_i32p, _c_u8p, ctypes.c_int, _c_i32p]
-        L.dmo_tree_walk.restype = ctypes.c_int
-        L.dmo_run.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Result)]
-        L.dmo_run.restype = ctypes.c_int
-        _lib = L
+        _lib = load(_LIB)
     return _lib
 
 
@@ -196,7 +203,7 @@ def tree_walk(parent, flags):
 # -------------------------------------------------------------- full verify
 def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False,
         want_masks=False, n_threads=None, temperature=0.0, top_k=0, top_p=0.0, seq_gamma=None, seq_K=None,
-        seq_p_drop=None, tree_parent=None):
+        seq_p_drop=None, tree_parent=None, library=None):
     """Run the verify step for the listed sequences (all by default).
 
     W: [V, d], h: [B, gamma+1, d] (float32 or uint16 bf16 bits, same dtype);
@@ -205,7 +212,9 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
     top_k / top_p (0 = off) process the lossless target.  seq_gamma /
     seq_K / seq_p_drop ([B] or None) make the batch ragged.  tree_parent
     (int32 [B, gamma]) gives the parent position of every draft of the
-    TREE_NAIVE sequences (a chain is parent[t] = t).  Returns a dict
+    TREE_NAIVE sequences (a chain is parent[t] = t).  `library`: a library
+    from load() to run instead of the oracle (the tests' planted-mistake
+    copies).  Returns a dict
     of numpy arrays whose leading dimension indexes the listed sequences.
     """
     W = np.ascontiguousarray(W)
@@ -274,7 +283,7 @@ def run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, want_logits=False
                     seq_gamma=_ptr(rg, _c_i32p), seq_K=_ptr(rk, _c_i32p), seq_p_drop=_ptr(rp, _c_f32p),
                     tree_parent=_ptr(tp, _c_i32p))
     res = _Result(**{name: _ptr(out.get(name), ctype) for name, ctype in _Result._fields_})
-    rc = lib().dmo_run(ctypes.byref(prob), ctypes.byref(res))
+    rc = (library or lib()).dmo_run(ctypes.byref(prob), ctypes.byref(res))
     if rc != 0:
         raise RuntimeError(f"oracle returned status {rc}")
     return out

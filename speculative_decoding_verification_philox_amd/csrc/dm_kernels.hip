@@ -1136,13 +1136,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
 // k_combine: final (max, log Z, argmax) per head row and per centroid.
 // One block per target: threads merge the per-vocabulary-group partials
 // (four loads in flight each), then a butterfly per wave and a fixed-order
-// merge of the waves, so repeated runs give identical bits.
+// merge of the waves, so repeated runs give identical bits.  Block 0 also
+// zeroes the call's residual-race slots, which k_vocab fills next: every
+// call starts from empty slots whatever an earlier call left there.
 // =====================================================================
 constexpr int kCombineThreads = 256;
 
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const Stat* __restrict__ part,
                                                              RowStat* __restrict__ rowstat,
                                                              RowStat* __restrict__ centstat,
+                                                             unsigned long long* __restrict__ race_best,
                                                              int32_t* __restrict__ dbg_head_arg,
                                                              float* __restrict__ dbg_head_logz,
                                                              int32_t* __restrict__ dbg_cent_arg,
@@ -1150,6 +1153,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
     __shared__ Stat s_w[kCombineThreads / 64];
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (t == 0)
+        for (int i = threadIdx.x; i < 2 * P.B; i += kCombineThreads) race_best[i] = 0ull;
     int b, pos_t, head = 0;
     const bool is_row = t < P.R_phys;
     bool lossless = false;
@@ -1498,8 +1503,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 // drafted position (lane t decides position t), finds the first rejection A
 // ("Speculative Decoding: Draft, Then Verify", the draft-then-verify loop,
 // steps 3 and 4) and emits one token: the centroid argmax at A for the
-// DropMatch rules, the race winner for lossless sequences (whose race slots
-// it then clears for the next call).
+// DropMatch rules, the race winner for lossless sequences.
 //
 // The kernel is latency-bound, so it is built around few memory round trips:
 // what the decisions read that does not depend on the JS sums (draft tokens,
@@ -1632,8 +1636,6 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
         if (lossless) {
             const unsigned long long best = best_r ? best_r : best_p;
             out_token[b] = best ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : 0;
-            race_best[2 * b] = 0ull;
-            race_best[2 * b + 1] = 0ull;
         } else {
             out_token[b] = token_lossy;
         }
@@ -2106,11 +2108,12 @@ hipError_t launch_gemm(const Plan& P, const void* W, const void* Hm, const RowMe
 
 int skinny_strips_per_group() { return kSkinnyNS * kSkinnyWaves; }
 
-hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, RowStat* centstat, int32_t* dbg_head_arg,
-                          float* dbg_head_logz, int32_t* dbg_cent_arg, float* dbg_cent_logz, hipStream_t st) {
+hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, RowStat* centstat,
+                          unsigned long long* race_best, int32_t* dbg_head_arg, float* dbg_head_logz,
+                          int32_t* dbg_cent_arg, float* dbg_cent_logz, hipStream_t st) {
     const int n = P.R_phys + P.n_lossy_pos;
-    hipLaunchKernelGGL(k_combine, dim3(n), dim3(kCombineThreads), 0, st, P, part, rowstat, centstat, dbg_head_arg,
-                       dbg_head_logz, dbg_cent_arg, dbg_cent_logz);
+    hipLaunchKernelGGL(k_combine, dim3(n), dim3(kCombineThreads), 0, st, P, part, rowstat, centstat, race_best,
+                       dbg_head_arg, dbg_head_logz, dbg_cent_arg, dbg_cent_logz);
     return hipGetLastError();
 }
 

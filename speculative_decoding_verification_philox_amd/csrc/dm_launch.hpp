@@ -11,8 +11,9 @@ hipError_t launch_prep(const Plan& P, const void* h, void* Hm, RowMeta* meta, ui
 hipError_t launch_pack_w(const void* W, void* Wp, int V, int nkb, size_t n16, hipStream_t st);
 hipError_t launch_gemm(const Plan& P, const void* W, const void* Hm, const RowMeta* meta, float* logits, Stat* part,
                        hipStream_t st);
-hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, RowStat* centstat, int32_t* dbg_head_arg,
-                          float* dbg_head_logz, int32_t* dbg_cent_arg, float* dbg_cent_logz, hipStream_t st);
+hipError_t launch_combine(const Plan& P, const Stat* part, RowStat* rowstat, RowStat* centstat,
+                          unsigned long long* race_best, int32_t* dbg_head_arg, float* dbg_head_logz,
+                          int32_t* dbg_cent_arg, float* dbg_cent_logz, hipStream_t st);
 hipError_t launch_filter(const Plan& P, const float* logits, const RowStat* rowstat, FiltStat* filt,
                          int32_t* dbg_count, float* dbg_logz, hipStream_t st);
 hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat, const int32_t* tree_parent,

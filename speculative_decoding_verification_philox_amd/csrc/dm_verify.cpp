@@ -324,15 +324,6 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
     h->jspart = (float*)take(s.jspart);
     h->race = (unsigned long long*)take(s.race);
     h->filt = (FiltStat*)take(s.filt);
-    // The race winners start at zero; the kernel that consumes them clears
-    // them at the end of every call.
-    e = hipMemset(h->race, 0, s.race);
-    if (e != hipSuccess) {
-        (void)hipFree(h->ws);
-        delete h;
-        (void)hipGetLastError();
-        return DM_ERR_HIP;
-    }
     h->cap_hm = s.hm;
     h->cap_meta_rows = s.meta / sizeof(RowMeta);
     h->cap_part = s.part;
@@ -453,8 +444,8 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
         DM_TRY(hipEventRecord(h->prof_stop, st));
         h->prof_start = h->prof_stop = nullptr;
     }
-    DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, a->head_argmax, a->head_logz, a->centroid_argmax,
-                          a->centroid_logz, st));
+    DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, h->race, a->head_argmax, a->head_logz,
+                          a->centroid_argmax, a->centroid_logz, st));
     DM_TRY(launch_filter(P, logits, h->rowstat, h->filt, a->filter_count, a->filter_logz, st));
     DM_TRY(launch_vocab(P, a->draft, a->q_hat, a->tree_parent, logits, h->rowstat, h->centstat, h->jspart, h->race,
                         h->filt, a->accept_len, a->out_token, a->accept_pos, a->data_status, a->accept_flags,

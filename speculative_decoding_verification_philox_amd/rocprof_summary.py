@@ -3,6 +3,9 @@
   python -m speculative_decoding_verification_philox_amd.rocprof_summary stats \
       RUN_kernel_stats.csv --command "..." --title "..." > profiles/X.md
 
+  python -m speculative_decoding_verification_philox_amd.rocprof_summary trace \
+      RUN_kernel_trace.csv --warmup W --command "..." --title "..." > profiles/X.md
+
   python -m speculative_decoding_verification_philox_amd.rocprof_summary traffic \
       --fetch FETCH_counter_collection.csv --write WRITE_counter_collection.csv \
       --kernel k_gemm_panel --workload llama3_8b_head --alg-bytes N \
@@ -51,12 +54,10 @@ def kernel_section(kernel: str) -> str:
 
 def kernel_source_hash(kernel: str | None = None) -> str:
     """sha256 (first 16 hex digits) of the whole kernel file, or, for one
-    kernel, of its section plus the shared header it includes."""
-    if kernel is None:
-        data = open(KERNEL_SRC, "rb").read()
-    else:
-        data = (kernel_section(kernel) + open(COMMON_SRC).read()).encode()
-    return hashlib.sha256(data).hexdigest()[:16]
+    kernel, of its section; either way followed by the shared header every
+    kernel includes (the Philox rounds, the row layout, the statistics)."""
+    body = open(KERNEL_SRC).read() if kernel is None else kernel_section(kernel)
+    return hashlib.sha256((body + open(COMMON_SRC).read()).encode()).hexdigest()[:16]
 
 
 def _short(name: str) -> str:
@@ -72,7 +73,32 @@ def stats(args) -> None:
     for r in rows:
         print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
               f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    print(f"\nKernel source sha256 (first 16 hex digits): `{kernel_source_hash()}`")
+    print(f"\nKernel source sha256 (first 16 hex digits) of csrc/dm_kernels.hip plus csrc/dm_common.hpp: "
+          f"`{kernel_source_hash()}`")
+
+
+def trace(args) -> None:
+    """Per-kernel durations from the kernel-trace records, leaving out the
+    first `--warmup` dispatches of every kernel launched more often than that
+    (the untimed warm-up steps), so the table shows the timed steps only."""
+    per: dict[str, list[float]] = {}
+    for r in csv.DictReader(open(args.csv)):
+        us = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
+        per.setdefault(_short(r["Kernel_Name"]), []).append(us)
+    timed = {k: (v[args.warmup:] if len(v) > args.warmup else v) for k, v in per.items()}
+    total = sum(sum(v) for v in timed.values())
+    print(f"# {args.title}\n")
+    print(f"Command (from the repository root):\n\n```\n{args.command}\n```\n")
+    print(f"The first {args.warmup} dispatches of each kernel launched more than {args.warmup} times are the "
+          f"warm-up steps and are left out; the other columns cover the remaining dispatches.\n")
+    print("| kernel | dispatches | timed | mean (us) | median (us) | min (us) | max (us) | share of timed GPU time |")
+    print("|---|---|---|---|---|---|---|---|")
+    for k in sorted(timed, key=lambda k: -sum(timed[k])):
+        v = timed[k]
+        print(f"| `{k}` | {len(per[k])} | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | "
+              f"{min(v):.1f} | {max(v):.1f} | {100.0 * sum(v) / total:.2f}% |")
+    print(f"\nKernel source sha256 (first 16 hex digits) of csrc/dm_kernels.hip plus csrc/dm_common.hpp: "
+          f"`{kernel_source_hash()}`")
 
 
 def _per_dispatch(path: str) -> dict[str, list[float]]:
@@ -171,6 +197,11 @@ def main(argv=None) -> None:
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
+    k = sub.add_parser("trace")
+    k.add_argument("csv")
+    k.add_argument("--warmup", type=int, required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--title", required=True)
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernel", required=True)
@@ -187,7 +218,7 @@ def main(argv=None) -> None:
     t.add_argument("--command", required=True)
     t.add_argument("--json", default=None)
     a = ap.parse_args(argv)
-    {"stats": stats, "counters": counters, "traffic": traffic}[a.cmd](a)
+    {"stats": stats, "trace": trace, "counters": counters, "traffic": traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":

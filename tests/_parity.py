@@ -11,11 +11,12 @@ Parity bar (from the verify step's contract):
     filter margin (logit gap at the k-th value, mass gap at the top-p
     boundary) is below 2e-3; such positions also exempt their decision and,
     at A, the emitted token.
-An argmax (or emitted token) may differ only where the oracle's top-2 gap is
-below the same 1e-4 (the fp32 path cannot order closer values reliably);
-those are counted too.  On a token tree any decision can move the kept path,
-so a sequence with a near-tie decision anywhere is exempt from the result
-check (and counted).
+An argmax (or emitted token) that differs where the oracle's top-2 gap is
+below the same 1e-4 is counted rather than failed at once, and so is a
+sequence whose result a near-tie decides (on a token tree any decision can
+move the kept path, so a near-tie anywhere counts there); assert_caps then
+holds every test to the bar: no argmax differs at all, and the differing
+decisions and sequences stay at or below 0.1%.
 """
 from __future__ import annotations
 
@@ -128,6 +129,7 @@ class Report:
     argmax_near_tie_mismatch: int = 0
     sequences: int = 0
     sequence_exempt: int = 0
+    sequence_mismatch_exempt: int = 0
     max_logit_err: float = 0.0
     max_js_err: float = 0.0
     max_logz_err: float = 0.0
@@ -230,7 +232,13 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False, rag
         else:
             tok_near = ora["centroid_gap"][r][pos_o] < MARGIN
         if decisive or tok_near:
+            # a near-tie decides this sequence: it is still compared, and a
+            # difference is counted (and capped by the caller), not failed
             rep.sequence_exempt += 1
+            same = int(gpu["accept_len"][b]) == A_o and int(gpu["out_token"][b]) == int(ora["out_token"][r])
+            if "accept_pos" in gpu:
+                same = same and int(gpu["accept_pos"][b]) == pos_o
+            rep.sequence_mismatch_exempt += 0 if same else 1
             continue
         assert int(gpu["accept_len"][b]) == A_o, f"accept_len of sequence {b}: gpu {gpu['accept_len'][b]} oracle {A_o}"
         if "accept_pos" in gpu:
@@ -239,6 +247,20 @@ def compare(gpu, ora, modes, K, seqs=None, check_debug=True, filtered=False, rag
         assert int(gpu["out_token"][b]) == int(ora["out_token"][r]), (
             f"out_token of sequence {b}: gpu {gpu['out_token'][b]} oracle {ora['out_token'][r]}")
     return rep
+
+
+def assert_caps(rep: Report, what: str = "") -> None:
+    """The bar on what near-ties may excuse, over a whole test: argmaxes are
+    bit-exact (no difference at all, near-tie or not); decisions and whole
+    sequences may differ only where the oracle's margin is below 1e-4, and
+    such differences must stay at or below 0.1% of the decisions (of the
+    sequences).  The near-tie counts themselves are reported."""
+    print(f"  near-tie accounting {what}: {rep}", flush=True)
+    assert rep.argmax_near_tie_mismatch == 0, f"{rep.argmax_near_tie_mismatch} argmaxes differ {what}"
+    assert rep.decision_mismatch_exempt <= rep.decisions // 1000, (
+        f"{rep.decision_mismatch_exempt} of {rep.decisions} decisions differ at near-ties {what}")
+    assert rep.sequence_mismatch_exempt <= rep.sequences // 1000, (
+        f"{rep.sequence_mismatch_exempt} of {rep.sequences} near-tie sequences differ {what}")
 
 
 def oracle_run(W, h, draft, q_hat, modes, K, p_drop, seed, seqs=None, debug=True, sampling=None, ragged=None,

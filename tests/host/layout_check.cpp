@@ -14,8 +14,10 @@ hipError_t launch_pack_w(const void*, void*, int, int, size_t, hipStream_t) { re
 hipError_t launch_gemm(const Plan&, const void*, const void*, const RowMeta*, float*, Stat*, hipStream_t) {
     return hipSuccess;
 }
-hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, int32_t*, float*, int32_t*, float*,
-                          hipStream_t) { return hipSuccess; }
+hipError_t launch_combine(const Plan&, const Stat*, RowStat*, RowStat*, unsigned long long*, int32_t*, float*,
+                          int32_t*, float*, hipStream_t) {
+    return hipSuccess;
+}
 hipError_t launch_filter(const Plan&, const float*, const RowStat*, FiltStat*, int32_t*, float*, hipStream_t) {
     return hipSuccess;
 }

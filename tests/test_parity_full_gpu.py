@@ -1,11 +1,18 @@
 """GPU parity at the workloads' full sizes (the five chain workloads and the
-token tree at the 70B head).
+token tree at the 70B head), over Philox seeds 1..20.
 
-Each test runs the library on the same inputs with W in both orders
-(row-major and panels), each twice: once exactly as bench.py times it (no
-inspection outputs), once with every inspection output on.  The oracle evaluates whole sequences (a sequence's outputs depend only
-on its own rows), all of them for B = 1 and a sample for the batched
-workloads; both GPU runs must agree with it."""
+For every seed the library runs on the same inputs exactly as bench.py times
+it (panel-order W, no inspection outputs) and once more with every
+inspection output on, and also with row-major W; all three runs must agree
+with the oracle.  The oracle evaluates whole sequences (a sequence's outputs
+depend only on its own rows): the only sequence at B = 1, and at the batched
+workloads a window that moves with the seed, so that over the 20 seeds every
+sequence of the batch -- hence every row tile and every lane-group slot of
+the layout -- is compared at least once.  Per workload the near-tie
+accounting is held to the bar (tests/_parity.py, assert_caps): no argmax
+differs, and decisions or sequences that differ at oracle near-ties stay at
+or below 0.1%.
+"""
 import numpy as np
 import pytest
 
@@ -14,6 +21,8 @@ from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
 
+SEEDS = range(1, 21)
+
 
 @pytest.fixture(scope="module", autouse=True)
 def need_gpu():
@@ -21,47 +30,62 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def _full(cfg_index, seqs, p_values=None, seeds=(None,)):
+def window(B, per_seed):
+    """Sequences the oracle evaluates for each seed: `per_seed` consecutive
+    ones, the window moving by `per_seed` per seed (wrapping)."""
+    return lambda seed: [(seed * per_seed + k) % B for k in range(per_seed)]
+
+
+def _full(cfg_index, per_seed=1, p_values=None, seeds=SEEDS):
     w = wl.generate(cfg_index)
     cfg = w.cfg
     print(f"  {cfg.name}: B={cfg.B} d={cfg.d} V={cfg.V} K={cfg.K}", flush=True)
     ver = P.make_verifier(w.W, w.h, cfg.K)
     inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
+    pick = window(cfg.B, per_seed)
     rep = P.Report()
+    covered = set()
     for p in (p_values or [cfg.p_drop]):
         for seed in seeds:
-            seed = wl.perf_seed(cfg.index) if seed is None else seed
-            print(f"  p_drop={p} seed={seed:#x} oracle sequences={list(seqs)}", flush=True)
+            seqs = pick(seed)
+            covered.update(seqs)
+            print(f"  p_drop={p} seed={seed} oracle sequences={seqs}", flush=True)
             o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs, tree=w.tree_parent)
-            for layout in P.LAYOUTS:
-                g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=layout,
-                                    tree=w.tree_parent)
-                g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=layout, tree=w.tree_parent)
-                for k in ("accept_len", "accept_pos", "out_token"):
-                    np.testing.assert_array_equal(g_bench[k], g_dbg[k], err_msg=k)
-                rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
-                rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
+            g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=P.PANELS,
+                                tree=w.tree_parent)
+            g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=P.PANELS, tree=w.tree_parent)
+            g_row = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=P.ROW_MAJOR,
+                              tree=w.tree_parent)
+            for k in ("accept_len", "accept_pos", "out_token"):
+                np.testing.assert_array_equal(g_bench[k], g_dbg[k], err_msg=k)
+            rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
+            rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
+            rep.add(P.compare(g_row, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
     ver.close()
-    print(rep, flush=True)
+    assert covered == set(range(cfg.B)), f"sequences never compared: {sorted(set(range(cfg.B)) - covered)}"
+    P.assert_caps(rep, f"({cfg.name})")
     return rep
 
 
 def test_config1_llama3_8b_head():
-    _full(1, seqs=[0], seeds=(None, 1, 2))
+    _full(1)
 
 
-def test_config2_llama31_70b_head_pdrop_sweep():
-    _full(2, seqs=[0], p_values=[0.1, 0.2, 0.3])
+@pytest.mark.parametrize("p_drop", [0.1, 0.2, 0.3])
+def test_config2_llama31_70b_head_pdrop_sweep(p_drop):
+    _full(2, p_values=[p_drop])
 
 
-def test_config3_batched_70b_sampled():
-    _full(3, seqs=[0, 13, 31])
+def test_config3_batched_70b():
+    # 2 sequences per seed: 40 over the 20 seeds, all 32 covered
+    _full(3, per_seed=2)
 
 
-def test_config4_wide_mixed_sampled():
-    _full(4, seqs=[0, 31, 32, 63])
+def test_config4_wide_mixed():
+    # 4 per seed: 80 over the 20 seeds, all 64 (both rules) covered
+    _full(4, per_seed=4)
 
 
 def test_config5_eagle3_70b_tree():
-    rep = _full(5, seqs=[0])
-    assert rep.sequences == 4
+    rep = _full(5)
+    assert rep.sequences == 3 * len(SEEDS)

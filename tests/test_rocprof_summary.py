@@ -97,3 +97,21 @@ def test_kernel_sections_are_separate(kernel):
     others = [k for k in ("k_gemm_panel", "k_gemm_tile", "k_vocab", "k_finish") if k != kernel]
     assert not any(RS._HEADER + o + ":" in sec for o in others)
     assert len(RS.kernel_source_hash(kernel)) == 16
+
+
+def test_trace_table_leaves_out_the_warmup_dispatches(tmp_path, capsys):
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows, t = [], 0
+    # two warm-up steps (slow), then three timed ones; the weight reorder runs once
+    for us in (3000, 2900, 2200, 2210, 2190):
+        for name, dur in (("void dmv::k_gemm_tile<true, 10, 1>(dmv::Plan, ...)", us), ("dmv::k_combine", 9)):
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+            t += dur * 1000 + 100
+    rows.append({"Kernel_Name": "dmv::k_pack_w", "Start_Timestamp": t, "End_Timestamp": t + 900_000})
+    p = tmp_path / "run_kernel_trace.csv"
+    _write(p, fields, rows)
+    RS.main(["trace", str(p), "--warmup", "2", "--command", "cmd", "--title", "T"])
+    out = capsys.readouterr().out
+    assert "| `void dmv::k_gemm_tile<true, 10, 1>` | 5 | 3 | 2200.0 | 2200.0 | 2190.0 | 2210.0 |" in out
+    assert "| `dmv::k_pack_w` | 1 | 1 | 900.0 |" in out
+    assert RS.kernel_source_hash() in out
