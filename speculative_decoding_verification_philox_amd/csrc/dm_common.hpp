@@ -64,7 +64,7 @@ struct Plan {
     int store_all;
     // LM-head weight order: 0 row-major, 1 panels of 64 rows (dm_verify_pack_w)
     int w_packed;
-    int tile_kernel;  // panel-ordered W past one small tile: k_gemm_tile with this many row tiles per workgroup (1, 2); else 0
+    int tile_kernel;  // 1: panel-ordered W past one small tile (k_gemm_tile), else 0
     int nkb;       // 64-byte fragments per weight row (row bytes / 64)
     int n_panels;  // ceil(V / 64)
     // vocabulary split of the GEMM's statistic partials

@@ -7,9 +7,9 @@
 //                 panel of 64 vocabulary rows straight into MFMA operands,
 //                 with a softmax-statistics epilogue per row and per centroid
 //   k_gemm_tile   the same for many rows: four panels x one tile of up to
-//                 160 rows (four waves) or two of up to 80 (eight waves) per
-//                 workgroup, all waves filling an LDS ring and multiplying,
-//                 two workgroups per CU, XCD-aware order
+//                 160 rows per workgroup (a wave per panel), W streamed into
+//                 a register ring, the masked rows shared through an LDS
+//                 ring, two workgroups per CU, XCD-aware order
 //   k_gemm_skinny LM-head GEMM over row-major W (all rows of a tile in one
 //                 workgroup; W streamed from HBM straight into MFMA operands),
 //                 same epilogue
@@ -628,49 +628,48 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // k_gemm_tile: the LM head for many rows (the matrix-core-bound regime):
 // L[rho, v] = scale(rho) * sum_j W[v, j] * Hm[rho, j] (DropMatch Eq. (3)
 // with the shared head W).  One workgroup computes one group of four panels
-// (256 vocabulary columns) against WR row tiles of 16 * MSUB rows.
+// (256 vocabulary columns) against one row tile of 16 * MSUB rows; wave w
+// owns panel w of the group.
 //
-// Four waves per row tile; wave w owns panel w % 4 of the group and tile
-// w / 4, so each W fragment in LDS feeds WR waves and each masked-row
-// fragment four.  Every wave also loads: a stage is one 64-byte slice of the
-// reduction index (16 W fragments and WR x MSUB masked-row fragments of
-// 1 KiB), copied from global memory straight into a kTileNBUF-deep LDS ring
-// (direct global-to-LDS loads, 16 bytes per lane, one instruction per
-// fragment, the fragments dealt round-robin to the waves).  Per stage a wave
-// refills the slot freed at the last barrier, multiplies the current slot
-// (4 x MSUB v_mfma_f32_16x16x32_bf16, 16x16x4 for fp32), waits until its own
-// loads of the next stage have landed, and meets the others at one barrier.
-// The barrier is a bare s_barrier: the workgroup fence of an ordinary
-// barrier would also wait for the loads of the later stages still in
-// flight, which empties the ring every stage.
+// A stage is one 64-byte slice of the reduction index.  Its masked-row
+// fragments (MSUB of 1 KiB, each read by all four waves) are copied from
+// global memory straight into a D-deep LDS ring (direct global-to-LDS
+// loads, 16 bytes per lane, dealt round-robin to the waves).  Its weight
+// fragments are read by one wave only, so each wave streams its panel's four
+// fragments (4 KiB, already in operand order) from global memory straight
+// into a D-deep register ring: the weight never passes through LDS.  Every
+// wave issues the same loads at every stage (a wave short of a masked-row
+// fragment copies one into a spare LDS area; stages past the end re-read the
+// last one into slots never read), so every wait is an exact count.  Per
+// stage a wave issues the loads of the stage D - 1 ahead, multiplies the
+// current one (4 x MSUB v_mfma_f32_16x16x32_bf16; 16x16x4 for fp32), waits
+// until its loads of the next stage have landed and meets the other waves at
+// a bare s_barrier (the workgroup fence of an ordinary barrier would also
+// wait for the loads of the later stages still in flight).
 //
-// A 3-deep ring of stages of at most 26 KiB lets two workgroups share a CU
-// (78 KiB of LDS each), and each meets only its own barrier, so one feeds
-// the matrix cores while the other waits.  WR = 1 (tiles of up to 10
-// sub-tiles, one wave of each workgroup per SIMD) is the usual shape; WR = 2
-// (two tiles of 4 or 5 sub-tiles, eight waves, two of each workgroup per
-// SIMD) serves plans whose rows pack with less padding into smaller tiles.
-// Blocks are mapped so that the tiles sharing a panel group run together on
-// one XCD (workgroups go to the eight XCDs in turn), where the group's W is
-// read from HBM once and then from that XCD's L2.
+// Two workgroups share a CU, each meeting only its own barrier, so one feeds
+// the matrix cores while the other waits.  Blocks are mapped so that the
+// tiles sharing a panel group run together on one XCD (workgroups go to the
+// eight XCDs in turn), where the group's W is read from HBM once and then
+// from that XCD's L2.
 //
 // The epilogue (in the ring's memory): statistics per row and per centroid
 // over each wave's 64 columns, merged across the four panels into
 // part[target][panel group]; stored rows written.
 // =====================================================================
-constexpr int kTileColWaves = 4;  // 64-column panels per workgroup
-constexpr int kTileNBUF = 3;      // stages in the LDS ring
+constexpr int kTileWaves = 4;  // 64-column panels per workgroup, one wave each
 
-// WR row tiles of MSUB sub-tiles per workgroup
-template <int MSUB, int WR>
+// Stages in both rings (D - 1 in flight): the register ring of W holds D
+// stages of 16 VGPRs beside the 16 * MSUB accumulators.
+template <int MSUB>
 struct TileShape {
-    static constexpr int WAVES = kTileColWaves * WR;
-    static constexpr int NW = kTileColWaves * 4;  // W fragments per stage
-    static constexpr int NA = WR * MSUB;          // masked-row fragments per stage
-    static constexpr int NF = NW + NA;
-    static constexpr int NJ = (NF + WAVES - 1) / WAVES;  // most fragments one wave loads per stage
-    static constexpr int STAGE = NF * 1024;
-    static constexpr int LDS = kTileNBUF * STAGE;
+    static constexpr int D = MSUB >= 9 ? 3 : 4;
+    static constexpr int NA = (MSUB + kTileWaves - 1) / kTileWaves;  // masked-row loads per wave per stage
+    static constexpr int STAGE = MSUB * 1024;
+    static constexpr int SPARE = D * STAGE;  // where a wave short of a fragment loads one
+    static constexpr int RING = SPARE + 1024;
+    static constexpr int EPI = kTileWaves * 2 * 16 * MSUB * (int)sizeof(Stat) + 16 * MSUB * (int)sizeof(RowMeta);
+    static constexpr int LDS = RING > EPI ? RING : EPI;
 };
 
 #define DM_AS_GLOBAL __attribute__((address_space(1)))
@@ -693,71 +692,48 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <bool BF16, int MSUB, int WR>
-__global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
-                                                            const uint8_t* __restrict__ Hp,
-                                                            const RowMeta* __restrict__ meta,
-                                                            float* __restrict__ logits,
-                                                            Stat* __restrict__ part) {
-    using TS = TileShape<MSUB, WR>;
-    constexpr int ROWS = 16 * MSUB, G = 4, WC = kTileColWaves, NBUF = kTileNBUF, kTileWaves = TS::WAVES;
-    constexpr int NW = TS::NW, NF = TS::NF, NJ = TS::NJ;
-    constexpr size_t ST_BYTES = (size_t)WR * WC * 2 * ROWS * sizeof(Stat);
-    static_assert(ST_BYTES + WR * ROWS * sizeof(RowMeta) <= (size_t)TS::LDS, "epilogue fits in the ring");
-    static_assert(NJ * (NBUF - 2) < 64, "vmcnt range");
+template <bool BF16, int MSUB>
+__global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, const uint8_t* __restrict__ Wp,
+                                                                  const uint8_t* __restrict__ Hp,
+                                                                  const RowMeta* __restrict__ meta,
+                                                                  float* __restrict__ logits,
+                                                                  Stat* __restrict__ part) {
+    using TS = TileShape<MSUB>;
+    constexpr int ROWS = 16 * MSUB, G = 4, D = TS::D, NA = TS::NA;
+    constexpr size_t ST_BYTES = (size_t)kTileWaves * 2 * ROWS * sizeof(Stat);
     __shared__ __align__(16) uint8_t ring[TS::LDS];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_groups = (P.n_panels + 3) >> 2;
-    const int n_pairs = (P.n_tiles + WR - 1) / WR;
     const int per_xcd = (n_groups + 7) >> 3;
     const int xcd = blockIdx.x & 7, k_local = blockIdx.x >> 3;
-    const int group = xcd * per_xcd + k_local / n_pairs;
-    const int pair = k_local % n_pairs;
+    const int group = xcd * per_xcd + k_local / P.n_tiles;
+    const int tile = k_local % P.n_tiles;
     if (group >= n_groups) return;  // the whole block, before any barrier
     const int nkb = P.nkb;
-    const int wc = wave % WC, wr = wave / WC;
-    const int tile = pair * WR + wr;
-    const bool has_tile = tile < P.n_tiles;  // an odd tile count idles the last pair's second row of waves
-    const int my_panel = group * 4 + wc;
+    const int my_panel = group * 4 + wave;
+    // a panel past the last one streams the last panel; its products are never used
+    const uint8_t* wsrc = Wp + (size_t)min(my_panel, P.n_panels - 1) * nkb * (G * 1024) + lane * 16;
+    const uint8_t* asrc = Hp + (size_t)tile * nkb * TS::STAGE + lane * 16;
 
-    // This wave's share of every stage: fragments wave, wave + 8, ... (the
-    // four panels' W first, then both tiles' masked rows).  A missing panel
-    // or tile reads a valid one; its products are never used.
-    const uint8_t* src[NJ];
-    int stride[NJ];
+    v4u wr[D][G];
+    auto load_w = [&](int slot, int st) {
+        const uint8_t* s = wsrc + (size_t)min(st, nkb - 1) * (G * 1024);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int f = wave + kTileWaves * j;
-        if (f < NW) {
-            const int p = min(group * 4 + f / G, P.n_panels - 1);
-            src[j] = Wp + ((size_t)p * nkb * G + f % G) * 1024 + lane * 16;
-            stride[j] = G * 1024;
-        } else {
-            const int fa = f - NW;  // past the last fragment for some waves at j = NJ - 1: never issued
-            const int t = min(pair * WR + fa / MSUB, P.n_tiles - 1);
-            src[j] = Hp + ((size_t)t * nkb * MSUB + fa % MSUB) * 1024 + lane * 16;
-            stride[j] = MSUB * 1024;
-        }
-    }
-    const bool full_share = NF % kTileWaves == 0 || wave < NF % kTileWaves;  // NJ loads per stage, else NJ - 1
-    auto issue = [&](int st) {
-        uint8_t* base = ring + (st % NBUF) * TS::STAGE;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int f = wave + kTileWaves * j;
-            if (f < NF)
-                __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(src[j] + (size_t)st * stride[j]),
-                                                 (DM_AS_LDS void*)(base + f * 1024), 16, 0, 0);
-        }
+        for (int g = 0; g < G; ++g) wr[slot][g] = *(const v4u*)(s + g * 1024);
     };
-    // the stage after the current one has landed once at most the stages
-    // issued after it are in flight (NBUF - 2 of them after a refill; the
-    // tail waits for everything)
-    auto wait_next = [&](bool refilled) {
-        if (!refilled) wait_vmcnt<0>();
-        else if (full_share) wait_vmcnt<NJ * (NBUF - 2)>();
-        else wait_vmcnt<(NJ - 1) * (NBUF - 2)>();
+    // fragments wave, wave + 4, ... of stage st into ring slot st % D
+    auto load_a = [&](int st) {
+        const uint8_t* s = asrc + (size_t)min(st, nkb - 1) * TS::STAGE;
+        uint8_t* base = ring + (st % D) * TS::STAGE;
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+            const int f = wave + kTileWaves * j;
+            const bool real = f < MSUB;
+            __builtin_amdgcn_global_load_lds((const DM_AS_GLOBAL void*)(s + (real ? f : wave) * 1024),
+                                             (DM_AS_LDS void*)(real ? base + f * 1024 : ring + TS::SPARE), 16, 0,
+                                             0);
+        }
     };
 
     v4f acc[G][MSUB];
@@ -765,61 +741,59 @@ __global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const 
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
-
+    auto mma = [&](const v4u (&w)[G], const uint8_t* abase) {
+        // masked-row fragments one ahead: the next one's LDS read is in
+        // flight while the current one's products issue
+        v4u a_next = *(const v4u*)abase;
 #pragma unroll
-    for (int st = 0; st < NBUF - 1; ++st)
-        if (st < nkb) issue(st);
-    wait_next(NBUF - 1 < nkb);
-    ring_barrier();
-    for (int st = 0; st < nkb; ++st) {
-        const bool refill = st + NBUF - 1 < nkb;
-        if (refill) issue(st + NBUF - 1);
-        if (has_tile) {
-            const uint8_t* base = ring + (st % NBUF) * TS::STAGE + lane * 16;
-            const uint8_t* abase = base + (NW + wr * MSUB) * 1024;
-            v4u w[G];
+        for (int m = 0; m < MSUB; ++m) {
+            const v4u afr = a_next;
+            if (m + 1 < MSUB) a_next = *(const v4u*)(abase + (m + 1) * 1024);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(base + (wc * G + g) * 1024);
-            // masked-row fragments one ahead: the next one's LDS read is in
-            // flight while the current one's products issue
-            v4u a_next = *(const v4u*)abase;
+            for (int g = 0; g < G; ++g) {
+                if (BF16) {
+                    acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, afr), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
+                } else {
+                    const v4f a4 = __builtin_bit_cast(v4f, afr);
+                    const v4f b4 = __builtin_bit_cast(v4f, w[g]);
 #pragma unroll
-            for (int m = 0; m < MSUB; ++m) {
-                const v4u afr = a_next;
-                if (m + 1 < MSUB) a_next = *(const v4u*)(abase + (m + 1) * 1024);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    if (BF16) {
-                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(v8bf, afr), __builtin_bit_cast(v8bf, w[g]), acc[g][m], 0, 0, 0);
-                    } else {
-                        const v4f a4 = __builtin_bit_cast(v4f, afr);
-                        const v4f b4 = __builtin_bit_cast(v4f, w[g]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], acc[g][m], 0, 0, 0);
                 }
             }
         }
-        wait_next(refill);
-        ring_barrier();
-    }
+    };
 
-    // ---------------- epilogue (the ring is free: every load has landed) ----------------
-    Stat* s_st = reinterpret_cast<Stat*>(ring);  // [wr][wc][2 * ROWS]
-    RowMeta* s_meta = reinterpret_cast<RowMeta*>(ring + ST_BYTES);  // [wr][ROWS]
-    for (int r = threadIdx.x; r < WR * ROWS; r += blockDim.x) {
-        const int t = pair * WR + r / ROWS;
-        RowMeta mt{-1, 0.0f, 0, 0};
-        if (t < P.n_tiles) mt = meta[(size_t)t * ROWS + r % ROWS];
-        s_meta[r] = mt;
+    // One uniform loop: trips of D stages, so the register ring's slots are
+    // fixed.  Stage st issues the loads of stage st + D - 1 and multiplies
+    // stage st; the loop starts D - 1 stages early (loads only) and runs past
+    // the last stage (clamped loads, no products).  Without a separate
+    // prologue the compiler sees the same loads on every path into the loop,
+    // so its own waits for the register ring stay exact counts.
+    const int n_trips = (nkb + 2 * D - 2) / D;
+    for (int trip = 0; trip < n_trips; ++trip) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            const int st = trip * D + k - (D - 1);
+            load_w((k + D - 1) % D, st + D - 1);
+            load_a(st + D - 1);
+            if (st >= 0 && st < nkb) mma(wr[k], ring + (st % D) * TS::STAGE + lane * 16);
+            wait_vmcnt<(D - 2) * (G + NA)>();
+            ring_barrier();
+        }
     }
+    wait_vmcnt<0>();
+    __syncthreads();  // every load landed, every ring read done: the ring is free
+
+    // ---------------- epilogue ----------------
+    Stat* s_st = reinterpret_cast<Stat*>(ring);                     // [wave][2 * ROWS]
+    RowMeta* s_meta = reinterpret_cast<RowMeta*>(ring + ST_BYTES);  // [ROWS]
+    for (int r = threadIdx.x; r < ROWS; r += blockDim.x) s_meta[r] = meta[(size_t)tile * ROWS + r];
     __syncthreads();
-    Stat* my_st = s_st + (size_t)(wr * WC + wc) * 2 * ROWS;
-    if (has_tile) {
-        const RowMeta* my_meta = s_meta + wr * ROWS;
+    Stat* my_st = s_st + (size_t)wave * 2 * ROWS;
+    {
         const int grp = lane >> 4, c16 = lane & 15;
         const int col0 = my_panel * 64 + c16;
         bool ok[G];
@@ -834,7 +808,7 @@ __global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const 
                 // statistics reduced together
                 RowMeta mt[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mt[j] = my_meta[16 * m + 4 * grp + j];
+                for (int j = 0; j < 4; ++j) mt[j] = s_meta[16 * m + 4 * grp + j];
                 float x[4][G];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -854,8 +828,7 @@ __global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const 
                 row16_stats<4, G, FULL>(x, ok, col0, st);
                 if (c16 == 0) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        my_st[16 * m + 4 * grp + j] = mt[j].canon >= 0 ? st[j] : stat_empty();
+                    for (int j = 0; j < 4; ++j) my_st[16 * m + 4 * grp + j] = mt[j].canon >= 0 ? st[j] : stat_empty();
                 }
             }
             if (tile < P.tiles_lossy) {
@@ -873,19 +846,15 @@ __global__ __launch_bounds__(kTileColWaves * 64 * WR, 2) void k_gemm_tile(const 
     __syncthreads();
     // merge the four panels in panel order: part[target][panel group]
     const int npt = P.GR * P.ppg;
-    for (int u = threadIdx.x; u < WR * 2 * ROWS; u += blockDim.x) {
-        const int rw = u / (2 * ROWS), t = u % (2 * ROWS);
-        const int tl = pair * WR + rw;
-        if (tl >= P.n_tiles) continue;
-        const int nloc = ROWS + (tl < P.tiles_lossy ? npt : 0);
-        if (t >= nloc) continue;
-        const Stat* col = s_st + (size_t)rw * WC * 2 * ROWS + t;
+    const int nloc = ROWS + (tile < P.tiles_lossy ? npt : 0);
+    for (int t = threadIdx.x; t < nloc; t += blockDim.x) {
+        const Stat* col = s_st + t;
         Stat st = col[0];
 #pragma unroll
-        for (int c = 1; c < WC; ++c) st = stat_merge(st, col[(size_t)c * 2 * ROWS]);
-        int target = tl * ROWS + t;
+        for (int c = 1; c < kTileWaves; ++c) st = stat_merge(st, col[(size_t)c * 2 * ROWS]);
+        int target = tile * ROWS + t;
         if (t >= ROWS) {
-            const int p = tl * npt + (t - ROWS);
+            const int p = tile * npt + (t - ROWS);
             if (p >= P.n_lossy_pos) continue;
             target = P.R_phys + p;
         }
@@ -2066,29 +2035,19 @@ static hipError_t launch_skinny_t(const Plan& P, const void* W, const void* Hm, 
 template <bool BF16>
 static hipError_t launch_tile_t(const Plan& P, const void* Wp, const void* Hp, const RowMeta* meta, float* logits,
                                 Stat* part, hipStream_t st) {
-    const int WR = P.tile_kernel == 2 ? 2 : 1;  // row tiles per workgroup
     const int n_groups = (P.n_panels + 3) / 4;
     const int per_xcd = (n_groups + 7) / 8;
-    const int n_pairs = (P.n_tiles + WR - 1) / WR;
-    dim3 grid(8 * per_xcd * n_pairs), block(kTileColWaves * 64 * WR);
+    dim3 grid(8 * per_xcd * P.n_tiles), block(kTileWaves * 64);
     const uint8_t* w = (const uint8_t*)Wp;
     const uint8_t* a = (const uint8_t*)Hp;
-    if (WR == 2) {
-        switch (P.msub) {
-            case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-            case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5, 2>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     switch (P.msub) {
-        case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 6: hipLaunchKernelGGL((k_gemm_tile<BF16, 6, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10, 1>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 4: hipLaunchKernelGGL((k_gemm_tile<BF16, 4>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 5: hipLaunchKernelGGL((k_gemm_tile<BF16, 5>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 6: hipLaunchKernelGGL((k_gemm_tile<BF16, 6>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10>), grid, block, 0, st, P, w, a, meta, logits, part); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

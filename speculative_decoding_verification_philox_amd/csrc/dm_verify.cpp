@@ -35,6 +35,9 @@ struct dm_verify {
 namespace {
 
 constexpr int kGroupsPerTile = 4;
+// Planner weight of one tile of the matrix-core kernel, in rows: every tile
+// streams the whole weight slice of its panel group.
+constexpr double kTileFixedRows = 256.0;
 // The vocabulary pass splits a position into at most 256 chunks of 2048.
 constexpr int kMaxVocab = 256 * 2048;  // 16x16 MFMA output: four row groups per lane
 
@@ -141,41 +144,28 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         }
     }
     // Panel-ordered W with more rows than one small tile holds: the
-    // matrix-core kernel.  A workgroup of WR row tiles computes WR*MT x 256
-    // outputs from (WR*MT + 256) operand rows per fragment, so for each WR
-    // the cost of a sub-tile count is its workgroups times that, the operand
-    // rows fetched per fragment over the whole grid; the cheapest wins, ties
-    // going to the larger tile.  One tile per workgroup (4..10 sub-tiles,
-    // four waves) is the default; two tiles of 4..5 sub-tiles (eight waves,
-    // four per SIMD) run as fast per computed row and are taken when their
-    // smaller tiles cut the computed rows (padding included) by at least 5%.
+    // matrix-core kernel, one row tile of 4..10 sub-tiles per workgroup of
+    // four 64-column panels.  A sub-tile count costs its tiles times
+    // (rows per tile + kTileFixedRows): the rows computed, padding included,
+    // plus a fixed share per tile for the weight stream every tile reads;
+    // the cheapest wins, ties going to the larger tile.
     P.tile_kernel = 0;
     if (w_packed && best_tiles > 1) {
-        auto tiles_for = [&](int ms) {
+        double best_cost = 0.0;
+        best_ms = 0;
+        for (int ms = 4; ms <= 10; ++ms) {
             const int S = 4 * ms;
             const int ppg = S / K;  // >= 1: S >= 16 >= K
             const int tl = P.n_lossy_pos > 0 ? cdiv(P.n_lossy_pos, (long long)P.GR * ppg) : 0;
             const int tn = P.n_lossless_pos > 0 ? cdiv(P.n_lossless_pos, (long long)P.GR * S) : 0;
-            return tl + tn;
-        };
-        int ms_wr[3] = {0, 0, 0}, tiles_wr[3] = {0, 0, 0};
-        for (int wr = 1; wr <= 2; ++wr) {
-            double best_cost = 0.0;
-            for (int ms = 4; ms <= (wr == 1 ? 10 : 5); ++ms) {
-                const int t = tiles_for(ms);
-                const double cost = (double)((t + wr - 1) / wr) * (wr * 16.0 * ms + 256.0);
-                if (ms_wr[wr] == 0 || cost <= best_cost) {
-                    ms_wr[wr] = ms;
-                    tiles_wr[wr] = t;
-                    best_cost = cost;
-                }
+            const double cost = (double)(tl + tn) * (16.0 * ms + kTileFixedRows);
+            if (best_ms == 0 || cost <= best_cost) {
+                best_ms = ms;
+                best_tiles = tl + tn;
+                best_cost = cost;
             }
         }
-        const long long rows1 = (long long)tiles_wr[1] * 16 * ms_wr[1];
-        const long long rows2 = (long long)tiles_wr[2] * 16 * ms_wr[2];
-        P.tile_kernel = rows2 * 100 <= rows1 * 95 ? 2 : 1;
-        best_ms = ms_wr[P.tile_kernel];
-        best_tiles = tiles_wr[P.tile_kernel];
+        P.tile_kernel = 1;
     }
     P.msub = best_ms;
     P.MT = 16 * best_ms;
@@ -263,6 +253,117 @@ size_t total_bytes(const Sizes& s) {
            align_up(s.filt, a);
 }
 
+// Device buffers of one call.
+struct Workspace {
+    void* Hm;
+    float* logits;
+    Stat* part;
+    RowStat* rowstat;
+    RowStat* centstat;
+    RowMeta* meta;
+    float* jspart;
+    unsigned long long* race;
+    FiltStat* filt;
+};
+
+// Carves the buffers of `s` out of `base` in a fixed order, each 256-byte aligned.
+Workspace carve(uint8_t* base, const Sizes& s) {
+    uint8_t* p = base;
+    auto take = [&](size_t n) {
+        uint8_t* r = p;
+        p += align_up(n, 256);
+        return r;
+    };
+    Workspace w;
+    w.Hm = take(s.hm);
+    w.logits = (float*)take(s.logits);
+    w.part = (Stat*)take(s.part);
+    w.rowstat = (RowStat*)take(s.rowstat);
+    w.centstat = (RowStat*)take(s.centstat);
+    w.meta = (RowMeta*)take(s.meta);
+    w.jspart = (float*)take(s.jspart);
+    w.race = (unsigned long long*)take(s.race);
+    w.filt = (FiltStat*)take(s.filt);
+    return w;
+}
+
+// The call's plan from its (checked) arguments: row layout, work split,
+// sequence sets, scales, thresholds and the Philox key.
+void plan_call(const dm_verify_desc& D, const dm_verify_args* a, Plan& P) {
+    int n_lossless = 0, n_js = 0;
+    for (int b = 0; b < a->batch; ++b) {
+        n_lossless += a->modes[b] == DM_MODE_LOSSLESS;
+        n_js += a->modes[b] == DM_MODE_JS_MAJORITY;
+    }
+    make_plan(D, a->batch, a->K, n_lossless, n_js, (int)a->w_layout, P);
+    for (int b = 0; b < a->batch; ++b) {
+        if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
+        if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
+        if (a->modes[b] == DM_MODE_TREE_NAIVE) P.tree_bits[b >> 5] |= 1u << (b & 31);
+    }
+    // temperature divides every row: folded into the row scales
+    const double temp = a->temperature > 0.0f ? (double)a->temperature : 1.0;
+    P.scale = (float)(1.0 / ((1.0 - (double)a->p_drop) * temp));
+    P.scale_undropped = (float)(1.0 / temp);
+    P.top_k = a->top_k;
+    P.top_p = a->top_p;
+    // ragged batches: per-sequence drafts and heads, dropout by palette index
+    P.ragged = a->seq_gamma || a->seq_heads || a->seq_p_drop;
+    if (P.ragged) {
+        int n_p = 0;
+        float pal[kMaxDropValues];
+        for (int b = 0; b < a->batch; ++b) {
+            P.seq_gamma[b] = (uint8_t)(a->seq_gamma ? a->seq_gamma[b] : D.gamma);
+            P.seq_k[b] = (uint8_t)(a->seq_heads ? a->seq_heads[b] : a->K);
+            const float pb = a->seq_p_drop ? a->seq_p_drop[b] : a->p_drop;
+            int k = 0;
+            while (k < n_p && pal[k] != pb) ++k;
+            if (k == n_p) {  // at most kMaxDropValues: checked above
+                pal[n_p++] = pb;
+                P.p_thresh[k] = drop_threshold(pb);
+                P.p_scale[k] = (float)(1.0 / ((1.0 - (double)pb) * temp));
+            }
+            P.seq_pi[b] = (uint8_t)k;
+        }
+    }
+    P.filter = n_lossless > 0 && ((a->top_k > 0 && a->top_k < D.vocab) || (a->top_p > 0.0f && a->top_p < 1.0f));
+    P.inv_k = 1.0f / (float)a->K;
+    P.thresh = drop_threshold(a->p_drop);
+    P.key0 = (uint32_t)(a->seed & 0xffffffffu);
+    P.key1 = (uint32_t)(a->seed >> 32);
+    P.store_all = a->logits != nullptr;
+}
+
+// Enqueues the kernels of one planned call on `st` over workspace `w`;
+// `prof_start` / `prof_stop` (or null) bracket the GEMM launch.
+int enqueue(const dm_verify_desc& D, Plan& P, const Workspace& w, const dm_verify_args* a, hipStream_t st,
+            hipEvent_t prof_start, hipEvent_t prof_stop) {
+    float* logits = a->logits ? a->logits : w.logits;
+    P.vec4 = (D.vocab % 4 == 0) && aligned(a->q_hat, 16) && aligned(logits, 16);
+    const int T1 = P.T1;
+    hipError_t e = hipSuccess;
+#define DM_TRY(x)                               \
+    do {                                        \
+        e = (x);                                \
+        if (e != hipSuccess) return DM_ERR_HIP; \
+    } while (0)
+    if (a->head_argmax) DM_TRY(launch_fill_i32(a->head_argmax, a->batch * T1 * a->K, -1, st));
+    if (a->centroid_argmax && P.ragged) DM_TRY(launch_fill_i32(a->centroid_argmax, a->batch * T1, -1, st));
+    if (a->mask_bits) DM_TRY(launch_fill_i32((int32_t*)a->mask_bits, a->batch * T1 * a->K * (D.d / 32), 0, st));
+    DM_TRY(launch_prep(P, a->h, w.Hm, w.meta, a->mask_bits, st));
+    if (prof_start) DM_TRY(hipEventRecord(prof_start, st));
+    DM_TRY(launch_gemm(P, a->W, w.Hm, w.meta, logits, w.part, st));
+    if (prof_stop) DM_TRY(hipEventRecord(prof_stop, st));
+    DM_TRY(launch_combine(P, w.part, w.rowstat, w.centstat, w.race, a->head_argmax, a->head_logz, a->centroid_argmax,
+                          a->centroid_logz, st));
+    DM_TRY(launch_filter(P, logits, w.rowstat, w.filt, a->filter_count, a->filter_logz, st));
+    DM_TRY(launch_vocab(P, a->draft, a->q_hat, a->tree_parent, logits, w.rowstat, w.centstat, w.jspart, w.race,
+                        w.filt, a->accept_len, a->out_token, a->accept_pos, a->data_status, a->accept_flags,
+                        a->js_heads, a->js_draft, st));
+#undef DM_TRY
+    return DM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,21 +410,16 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out) {
         (void)hipGetLastError();
         return e == hipErrorOutOfMemory ? DM_ERR_OUT_OF_MEMORY : DM_ERR_HIP;
     }
-    uint8_t* p = h->ws;
-    auto take = [&](size_t n) {
-        uint8_t* r = p;
-        p += align_up(n, 256);
-        return r;
-    };
-    h->Hm = take(s.hm);
-    h->logits = (float*)take(s.logits);
-    h->part = (Stat*)take(s.part);
-    h->rowstat = (RowStat*)take(s.rowstat);
-    h->centstat = (RowStat*)take(s.centstat);
-    h->meta = (RowMeta*)take(s.meta);
-    h->jspart = (float*)take(s.jspart);
-    h->race = (unsigned long long*)take(s.race);
-    h->filt = (FiltStat*)take(s.filt);
+    const Workspace w = carve(h->ws, s);
+    h->Hm = w.Hm;
+    h->logits = w.logits;
+    h->part = w.part;
+    h->rowstat = w.rowstat;
+    h->centstat = w.centstat;
+    h->meta = w.meta;
+    h->jspart = w.jspart;
+    h->race = w.race;
+    h->filt = w.filt;
     h->cap_hm = s.hm;
     h->cap_meta_rows = s.meta / sizeof(RowMeta);
     h->cap_part = s.part;
@@ -369,89 +465,20 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     int rc = check_args(&h->desc, a);
     if (rc != DM_OK) return rc;
     const dm_verify_desc& D = h->desc;
-    hipStream_t st = (hipStream_t)stream;
-
     Plan P{};
-    int n_lossless = 0, n_js = 0;
-    for (int b = 0; b < a->batch; ++b) {
-        n_lossless += a->modes[b] == DM_MODE_LOSSLESS;
-        n_js += a->modes[b] == DM_MODE_JS_MAJORITY;
-    }
-    make_plan(D, a->batch, a->K, n_lossless, n_js, (int)a->w_layout, P);
-    for (int b = 0; b < a->batch; ++b) {
-        if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
-        if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
-        if (a->modes[b] == DM_MODE_TREE_NAIVE) P.tree_bits[b >> 5] |= 1u << (b & 31);
-    }
-    // temperature divides every row: folded into the row scales
-    const double temp = a->temperature > 0.0f ? (double)a->temperature : 1.0;
-    P.scale = (float)(1.0 / ((1.0 - (double)a->p_drop) * temp));
-    P.scale_undropped = (float)(1.0 / temp);
-    P.top_k = a->top_k;
-    P.top_p = a->top_p;
-    // ragged batches: per-sequence drafts and heads, dropout by palette index
-    P.ragged = a->seq_gamma || a->seq_heads || a->seq_p_drop;
-    if (P.ragged) {
-        int n_p = 0;
-        float pal[kMaxDropValues];
-        for (int b = 0; b < a->batch; ++b) {
-            P.seq_gamma[b] = (uint8_t)(a->seq_gamma ? a->seq_gamma[b] : D.gamma);
-            P.seq_k[b] = (uint8_t)(a->seq_heads ? a->seq_heads[b] : a->K);
-            const float pb = a->seq_p_drop ? a->seq_p_drop[b] : a->p_drop;
-            int k = 0;
-            while (k < n_p && pal[k] != pb) ++k;
-            if (k == n_p) {  // at most kMaxDropValues: checked above
-                pal[n_p++] = pb;
-                P.p_thresh[k] = drop_threshold(pb);
-                P.p_scale[k] = (float)(1.0 / ((1.0 - (double)pb) * temp));
-            }
-            P.seq_pi[b] = (uint8_t)k;
-        }
-    }
-    P.filter = n_lossless > 0 && ((a->top_k > 0 && a->top_k < D.vocab) || (a->top_p > 0.0f && a->top_p < 1.0f));
-    P.inv_k = 1.0f / (float)a->K;
-    P.thresh = drop_threshold(a->p_drop);
-    P.key0 = (uint32_t)(a->seed & 0xffffffffu);
-    P.key1 = (uint32_t)(a->seed >> 32);
-    P.store_all = a->logits != nullptr;
-    P.vec4 = (D.vocab % 4 == 0) && aligned(a->q_hat, 16) && aligned(a->logits ? (const void*)a->logits : h->logits, 16);
+    plan_call(D, a, P);
     // The workspace was sized for the worst plan of the desc; refuse a plan
     // that would not fit rather than launch past the end of a buffer.
     if ((size_t)P.R_phys * D.d * elem_size(D.dtype) > h->cap_hm || (size_t)P.R_phys > h->cap_meta_rows ||
         (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) > h->cap_part ||
         (size_t)P.n_js_pos * P.js_chunks * (P.K + 1) * sizeof(float) > h->cap_jspart)
         return DM_ERR_UNSUPPORTED;
-    float* logits = a->logits ? a->logits : h->logits;
-
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return DM_ERR_HIP;
-
-    const int T1 = P.T1;
-    hipError_t e = hipSuccess;
-#define DM_TRY(x)                          \
-    do {                                   \
-        e = (x);                           \
-        if (e != hipSuccess) return DM_ERR_HIP; \
-    } while (0)
-    if (a->head_argmax) DM_TRY(launch_fill_i32(a->head_argmax, a->batch * T1 * a->K, -1, st));
-    if (a->centroid_argmax && P.ragged) DM_TRY(launch_fill_i32(a->centroid_argmax, a->batch * T1, -1, st));
-    if (a->mask_bits) DM_TRY(launch_fill_i32((int32_t*)a->mask_bits, a->batch * T1 * a->K * (D.d / 32), 0, st));
-    DM_TRY(launch_prep(P, a->h, h->Hm, h->meta, a->mask_bits, st));
-    const bool prof = h->prof_start && h->prof_stop;
-    if (prof) DM_TRY(hipEventRecord(h->prof_start, st));
-    DM_TRY(launch_gemm(P, a->W, h->Hm, h->meta, logits, h->part, st));
-    if (prof) {
-        DM_TRY(hipEventRecord(h->prof_stop, st));
-        h->prof_start = h->prof_stop = nullptr;
-    }
-    DM_TRY(launch_combine(P, h->part, h->rowstat, h->centstat, h->race, a->head_argmax, a->head_logz,
-                          a->centroid_argmax, a->centroid_logz, st));
-    DM_TRY(launch_filter(P, logits, h->rowstat, h->filt, a->filter_count, a->filter_logz, st));
-    DM_TRY(launch_vocab(P, a->draft, a->q_hat, a->tree_parent, logits, h->rowstat, h->centstat, h->jspart, h->race,
-                        h->filt, a->accept_len, a->out_token, a->accept_pos, a->data_status, a->accept_flags,
-                        a->js_heads, a->js_draft, st));
-#undef DM_TRY
-    return DM_OK;
+    const Workspace w{h->Hm, h->logits, h->part, h->rowstat, h->centstat, h->meta, h->jspart, h->race, h->filt};
+    hipEvent_t ps = h->prof_start, pe = h->prof_stop;
+    h->prof_start = h->prof_stop = nullptr;  // armed for one run
+    return enqueue(D, P, w, a, (hipStream_t)stream, ps && pe ? ps : nullptr, ps && pe ? pe : nullptr);
 }
 
 }  // extern "C"

@@ -312,43 +312,38 @@ def test_dropout_extremes(p_drop, layout):
 
 # ------------------------------------------ the matrix-core tile kernel
 def _tile_choice(n_pos, K, n_lossless=0):
-    """(sub-tiles per tile, tiles, row tiles per workgroup) the library's
-    planner takes for panel-order W with n_pos lossy positions (K head rows
-    each, four lane groups of (4 * sub-tiles) // K positions per tile) and
-    n_lossless lossless positions (one row each, in tiles of their own):
-    64-row tiles first; past one of those, for one tile per workgroup
-    (4..10 sub-tiles) and for two (4..5), the fewest workgroups x (rows per
-    workgroup + 256), ties to the larger tile; two per workgroup when that
-    computes at least 5% fewer rows.  Used only to choose and label the cases
-    below."""
+    """(sub-tiles per tile, tiles) the library's planner takes for
+    panel-order W with n_pos lossy positions (K head rows each, four lane
+    groups of (4 * sub-tiles) // K positions per tile) and n_lossless
+    lossless positions (one row each, in tiles of their own): 64-row tiles
+    first; past one of those, the tile kernel with 4..10 sub-tiles, the
+    fewest tiles x (rows per tile + 256), ties to the larger tile.  Used only
+    to choose and label the cases below."""
     def tiles(ms):
         tl = -(-n_pos // (4 * ((4 * ms) // K))) if n_pos else 0
         return tl + (-(-n_lossless // (16 * ms)) if n_lossless else 0)
     small = min(tiles(ms) for ms in range(1, 5) if 4 * ms >= K or not n_pos)
     if small <= 1:
         return None
-    best = {wr: min(range(4, hi + 1), key=lambda ms: (-(-tiles(ms) // wr) * (wr * 16 * ms + 256), -ms))
-            for wr, hi in ((1, 10), (2, 5))}
-    rows = {wr: tiles(ms) * 16 * ms for wr, ms in best.items()}
-    wr = 2 if rows[2] * 100 <= rows[1] * 95 else 1
-    return best[wr], tiles(best[wr]), wr
+    ms = min(range(4, 11), key=lambda ms: (tiles(ms) * (16 * ms + 256), -ms))
+    return ms, tiles(ms)
 
 
-# (B, gamma, K, |V|): every (sub-tiles, row tiles per workgroup) instance of
-# the kernel, at one to nine tiles.  |V| = 1000 leaves four panel groups (the
-# last panel 40 columns wide), so four of the eight XCD slots idle;
-# |V| = 2100 leaves a ninth group holding one 52-column panel.
+# (B, gamma, K, |V|): every sub-tile count of the kernel from 5 to 10 (four:
+# the mixed-rule test below), at one to five tiles.  |V| = 1000 leaves four
+# panel groups (the last panel 40 columns wide), so four of the eight XCD
+# slots idle; |V| = 2100 leaves a ninth group holding one 52-column panel.
 TILE_CASES = [(1, 4, 9, 1000), (1, 12, 11, 2100), (2, 8, 14, 1000), (1, 12, 15, 2100), (5, 4, 11, 1000),
               (2, 8, 13, 2100), (3, 10, 15, 2100), (7, 6, 10, 2100), (5, 4, 13, 1000)]
 
 
 def test_tile_cases_cover_every_sub_tile_count():
     got = {_tile_choice(B * (G + 1), K) for B, G, K, _ in TILE_CASES}
-    assert {(c[0], c[2]) for c in got} == {(m, 1) for m in range(5, 11)} | {(4, 2), (5, 2)}
+    assert {c[0] for c in got} == set(range(5, 11))
     assert max(c[1] for c in got) >= 5
-    # four sub-tiles, one per workgroup: lossy and lossless rows each fill one 64-row tile
-    assert _tile_choice(8, 5, n_lossless=8) == (4, 2, 1)
-    assert _tile_choice(24, 8, n_lossless=24) == (4, 4, 2)
+    # four sub-tiles: lossy and lossless rows each fill one 64-row tile
+    assert _tile_choice(8, 5, n_lossless=8) == (4, 2)
+    assert _tile_choice(24, 8, n_lossless=24) == (6, 3)
 
 
 @pytest.mark.parametrize("B,gamma,K,V", TILE_CASES, ids=[f"B{b}g{g}K{k}V{v}" for b, g, k, v in TILE_CASES])
@@ -356,7 +351,7 @@ def test_tile_kernel_every_sub_tile_count(B, gamma, K, V):
     """Panel-order W at row counts that take each instance of the tile kernel,
     bf16, every sequence on the JS rule (the planned shape) and then on mixed
     rules (lossless rows in tiles of their own)."""
-    print(f"  tile plan (sub-tiles, tiles, row tiles per workgroup) = {_tile_choice(B * (gamma + 1), K)}", flush=True)
+    print(f"  tile plan (sub-tiles, tiles) = {_tile_choice(B * (gamma + 1), K)}", flush=True)
     w = wl.generate(1, B=B, gamma=gamma, d=320, V=V, K=K, planted=0.8)
     _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, range(1, 3), layout=P.PANELS)
     if B > 1:
@@ -368,20 +363,19 @@ def test_tile_kernel_four_sub_tiles_mixed_rules():
     """One JS and one lossless sequence of eight positions at K = 5: each
     rule's rows fill one 64-row tile, so the tile kernel runs with four
     sub-tiles and two tiles."""
-    assert _tile_choice(8, 5, n_lossless=8) == (4, 2, 1)
+    assert _tile_choice(8, 5, n_lossless=8) == (4, 2)
     w = wl.generate(1, B=2, gamma=7, d=320, V=1000, K=5, planted=0.8)
     modes = np.array([wl.JS, wl.LOSSLESS], np.uint8)
     _check(w.W, w.h, w.draft, w.q_hat, modes, 5, 0.2, range(1, 4), layout=P.PANELS)
 
 
-def test_tile_kernel_two_row_tiles_per_workgroup():
-    """Half lossless, half naive at K = 8 (24 positions of each): one tile
-    per workgroup would take three 96-row tiles (288 rows for 216 live ones),
-    four 64-row tiles take 256, at least 5% fewer, so the planner puts two
-    tiles in each workgroup of eight waves.  Panel-order W only: row-major W
-    never takes the tile kernel.  The same shape on the JS rule alone follows
-    as a one-tile-per-workgroup case."""
-    assert _tile_choice(24, 8, n_lossless=24) == (4, 4, 2)
+def test_tile_kernel_half_lossless_half_naive():
+    """Half lossless, half naive at K = 8 (24 positions of each, the wide
+    mixed workload's rule split): three tiles of six sub-tiles, 216 live rows
+    in 288 (the lossy rows fill two 96-row tiles exactly).  Panel-order W
+    only: row-major W never takes the tile kernel.  The same shape on the JS
+    rule alone follows."""
+    assert _tile_choice(24, 8, n_lossless=24) == (6, 3)
     w = wl.generate(1, B=8, gamma=5, d=320, V=2100, K=8, planted=0.8)
     modes = wl.modes_for(wl.CONFIGS[4], B=8)  # the first half lossless, the rest naive
     _check(w.W, w.h, w.draft, w.q_hat, modes, 8, 0.2, range(1, 3), layout=P.PANELS)
