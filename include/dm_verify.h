@@ -84,7 +84,8 @@ typedef enum dm_status {
     DM_ERR_INVALID_ARGUMENT = 1, /* NULL where required, value out of range */
     DM_ERR_UNSUPPORTED = 2,      /* valid but not handled: dtype, d % 64, alignment */
     DM_ERR_HIP = 3,              /* a HIP runtime call or a launch failed */
-    DM_ERR_OUT_OF_MEMORY = 4     /* workspace allocation failed */
+    DM_ERR_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
+    DM_ERR_TOO_LARGE = 5         /* dm_verify_run_static: the call needs more than the scratch array */
 } dm_status;
 
 typedef enum dm_dtype { DM_DTYPE_F32 = 0, DM_DTYPE_BF16 = 1 } dm_dtype;
@@ -188,6 +189,26 @@ int dm_verify_create(const dm_verify_desc* desc, dm_verify_t** out);
 /* Enqueues one verify step on `stream` (hipStream_t, NULL = null stream).
  * Validates every argument first; returns without enqueuing on error. */
 int dm_verify_run(dm_verify_t* handle, const dm_verify_args* args, void* stream);
+
+/* The same verify step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It needs no handle and calls no allocating routine: the
+ * workspace is a fixed device array of dm_verify_static_scratch_bytes()
+ * bytes (64 MiB) inside the library, one per GPU, held until the process
+ * ends.  `desc` gives the limits the handle's desc would (checked the same
+ * way); the arguments, outputs, stream behaviour and results are those of
+ * dm_verify_run with a handle created from `desc`.  The call's own
+ * workspace (masked rows, the fp32 logits of B * (gamma+1) * K rows, the
+ * statistics) must fit the array, else it returns DM_ERR_TOO_LARGE before
+ * any HIP call: the Llama-3.1-70B-shaped head at B = 1, gamma = 7, K = 5
+ * needs about 22 MB.  Every call on a GPU uses that GPU's one array: calls
+ * that overlap on one GPU (on different streams, or from several host
+ * threads) race and must be serialised by the caller.  Nothing has to be
+ * cleared between calls: each call zeroes what it accumulates. */
+int dm_verify_run_static(const dm_verify_desc* desc, const dm_verify_args* args, void* stream);
+
+/* Size in bytes of the fixed scratch array of dm_verify_run_static. */
+size_t dm_verify_static_scratch_bytes(void);
 
 /* Frees the workspace and the handle.  NULL is a no-op returning DM_OK. */
 int dm_verify_destroy(dm_verify_t* handle);

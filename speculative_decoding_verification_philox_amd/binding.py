@@ -19,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdmverify.so")
 
 DM_OK, DM_ERR_INVALID_ARGUMENT, DM_ERR_UNSUPPORTED, DM_ERR_HIP, DM_ERR_OUT_OF_MEMORY = 0, 1, 2, 3, 4
+DM_ERR_TOO_LARGE = 5
 DM_DTYPE_F32, DM_DTYPE_BF16 = 0, 1
 DM_MODE_LOSSLESS, DM_MODE_NAIVE, DM_MODE_JS_MAJORITY, DM_MODE_TREE_NAIVE = 0, 1, 2, 3
 DM_W_ROW_MAJOR, DM_W_PANELS = 0, 1
@@ -51,7 +52,8 @@ class dm_verify_args(ctypes.Structure):
 
 
 EXPORTS = ("dm_verify_create", "dm_verify_run", "dm_verify_destroy", "dm_verify_profile", "dm_verify_check",
-           "dm_verify_workspace_bytes", "dm_verify_status_string", "dm_verify_packed_w_bytes", "dm_verify_pack_w")
+           "dm_verify_workspace_bytes", "dm_verify_status_string", "dm_verify_packed_w_bytes", "dm_verify_pack_w",
+           "dm_verify_run_static", "dm_verify_static_scratch_bytes")
 
 _lib = None
 
@@ -80,6 +82,11 @@ def library() -> ctypes.CDLL:
         L.dm_verify_pack_w.argtypes = [ctypes.POINTER(dm_verify_desc), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
         L.dm_verify_pack_w.restype = ctypes.c_int
+        L.dm_verify_run_static.argtypes = [ctypes.POINTER(dm_verify_desc), ctypes.POINTER(dm_verify_args),
+                                           ctypes.c_void_p]
+        L.dm_verify_run_static.restype = ctypes.c_int
+        L.dm_verify_static_scratch_bytes.argtypes = []
+        L.dm_verify_static_scratch_bytes.restype = ctypes.c_size_t
         L.dm_verify_status_string.argtypes = [ctypes.c_int]
         L.dm_verify_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -122,6 +129,16 @@ def dm_verify_run(handle: ctypes.c_void_p, args: dm_verify_args, stream: int | N
     rc = library().dm_verify_run(handle, ctypes.byref(args), ctypes.c_void_p(stream or 0))
     if rc != DM_OK:
         raise DmError(rc, "dm_verify_run")
+
+
+def dm_verify_run_static(desc: dm_verify_desc, args: dm_verify_args, stream: int | None = None) -> None:
+    rc = library().dm_verify_run_static(ctypes.byref(desc), ctypes.byref(args), ctypes.c_void_p(stream or 0))
+    if rc != DM_OK:
+        raise DmError(rc, "dm_verify_run_static")
+
+
+def dm_verify_static_scratch_bytes() -> int:
+    return int(library().dm_verify_static_scratch_bytes())
 
 
 def dm_verify_profile(handle: ctypes.c_void_p, start_event: int | None, stop_event: int | None) -> None:
@@ -260,7 +277,7 @@ class Verifier:
 
     def run(self, W, h, draft, q_hat, modes, K, p_drop, seed, stream=None, debug=False, outputs=None,
             w_layout=DM_W_ROW_MAJOR, temperature=1.0, top_k=0, top_p=1.0, seq_gamma=None, seq_heads=None,
-            seq_p_drop=None, tree_parent=None):
+            seq_p_drop=None, tree_parent=None, no_alloc=False):
         """Enqueue one verify step on `stream` (default: torch's current stream).
 
         W is row-major [vocab, d] (w_layout=DM_W_ROW_MAJOR) or the uint8
@@ -271,7 +288,9 @@ class Verifier:
         gives the parent position of every draft of the TREE_NAIVE
         sequences.  Returns a dict with accept_len, accept_pos, out_token and
         data_status (and every debug output when debug=True).  Preallocated outputs can
-        be passed in `outputs`."""
+        be passed in `outputs`.  no_alloc=True enqueues the same step through
+        dm_verify_run_static (the library's fixed scratch array instead of this
+        handle's workspace)."""
         import torch
 
         D = self.desc
@@ -304,5 +323,8 @@ class Verifier:
                               data_status=out["data_status"], **dbg)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        dm_verify_run(self.handle, args, stream)
+        if no_alloc:
+            dm_verify_run_static(self.desc, args, stream)
+        else:
+            dm_verify_run(self.handle, args, stream)
         return out

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "dm_common.hpp"
@@ -253,6 +254,23 @@ size_t total_bytes(const Sizes& s) {
            align_up(s.filt, a);
 }
 
+// The workspace one planned call uses (the handle's is sized for the worst
+// plan of its desc instead).
+Sizes plan_sizes(const dm_verify_desc& D, const Plan& P) {
+    Sizes s{};
+    const size_t rows = (size_t)P.B * P.T1;
+    s.hm = (size_t)P.R_phys * D.d * elem_size(D.dtype);
+    s.logits = rows * P.K * D.vocab * sizeof(float);
+    s.part = (size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat);
+    s.rowstat = rows * P.K * sizeof(RowStat);
+    s.centstat = rows * sizeof(RowStat);
+    s.meta = (size_t)P.R_phys * sizeof(RowMeta);
+    s.jspart = ((size_t)P.n_js_pos * P.js_chunks * (P.K + 1) + 1) * sizeof(float);
+    s.race = (size_t)P.B * 2 * sizeof(unsigned long long);
+    s.filt = rows * sizeof(FiltStat);
+    return s;
+}
+
 // Device buffers of one call.
 struct Workspace {
     void* Hm;
@@ -364,6 +382,34 @@ int enqueue(const dm_verify_desc& D, Plan& P, const Workspace& w, const dm_verif
     return DM_OK;
 }
 
+// ---------------------------------------------------- fixed scratch array
+// dm_verify_run_static's workspace: a fixed device array, one per GPU, held
+// until the process ends, so that entry point allocates nothing.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or null on a HIP error.
+void* scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -375,6 +421,7 @@ const char* dm_verify_status_string(int status) {
         case DM_ERR_UNSUPPORTED: return "unsupported";
         case DM_ERR_HIP: return "HIP runtime error";
         case DM_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case DM_ERR_TOO_LARGE: return "the call's workspace exceeds the fixed scratch array";
         default: return "unknown status";
     }
 }
@@ -479,6 +526,24 @@ int dm_verify_run(dm_verify_t* h, const dm_verify_args* a, void* stream) {
     hipEvent_t ps = h->prof_start, pe = h->prof_stop;
     h->prof_start = h->prof_stop = nullptr;  // armed for one run
     return enqueue(D, P, w, a, (hipStream_t)stream, ps && pe ? ps : nullptr, ps && pe ? pe : nullptr);
+}
+
+size_t dm_verify_static_scratch_bytes(void) { return kScratchBytes; }
+
+int dm_verify_run_static(const dm_verify_desc* desc, const dm_verify_args* a, void* stream) {
+    int rc = check_desc(desc);
+    if (rc != DM_OK) return rc;
+    rc = check_args(desc, a);
+    if (rc != DM_OK) return rc;
+    Plan P{};
+    plan_call(*desc, a, P);
+    const Sizes s = plan_sizes(*desc, P);
+    if (total_bytes(s) > kScratchBytes) return DM_ERR_TOO_LARGE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DM_ERR_HIP;
+    uint8_t* base = (uint8_t*)scratch_address(dev);
+    if (!base) return DM_ERR_HIP;
+    return enqueue(*desc, P, carve(base, s), a, (hipStream_t)stream, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -100,16 +100,17 @@ def weights(ver, inp: Inputs, layout):
 
 
 def run_gpu(ver, inp: Inputs, modes, K, p_drop, seed, debug=True, layout=ROW_MAJOR, sampling=None, ragged=None,
-            tree=None):
+            tree=None, no_alloc=False):
     """`ragged`: dict of seq_gamma / seq_heads / seq_p_drop host arrays;
-    `tree`: int32 [B, gamma] parent positions (copied to the device)."""
+    `tree`: int32 [B, gamma] parent positions (copied to the device);
+    `no_alloc`: through dm_verify_run_static instead of the handle."""
     import torch
 
     tp = None
     if tree is not None and inp.h.shape[1] > 1:
         tp = to_device(np.ascontiguousarray(tree, dtype=np.int32))
     out = ver.run(weights(ver, inp, layout), inp.h, inp.draft, inp.q_hat, modes, K, p_drop, seed, debug=debug,
-                  w_layout=layout, tree_parent=tp, **(sampling or {}), **(ragged or {}))
+                  w_layout=layout, tree_parent=tp, no_alloc=no_alloc, **(sampling or {}), **(ragged or {}))
     torch.cuda.synchronize()
     res = {}
     for k, v in out.items():

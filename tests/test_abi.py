@@ -210,7 +210,7 @@ def test_workspace_grows_with_limits(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert B.dm_verify_status_string(s) not in ("", "unknown status")
     assert B.dm_verify_status_string(99) == "unknown status"
 
@@ -235,3 +235,18 @@ def test_pack_w_rejects_bad_arguments_on_the_host(lib):
     bad = desc(d=100)
     assert lib.dm_verify_pack_w(ctypes.byref(bad), ctypes.c_void_p(base), ctypes.c_void_p(base),
                                 None) == B.DM_ERR_UNSUPPORTED
+
+
+def test_static_entry_rejects_on_the_host(lib):
+    """dm_verify_run_static checks the desc, the arguments and the size of
+    the call's workspace against its fixed scratch array before any HIP call
+    (the fake pointers are never touched)."""
+    assert B.dm_verify_static_scratch_bytes() == 64 << 20
+    run = lib.dm_verify_run_static
+    assert run(None, ctypes.byref(args()), None) == B.DM_ERR_INVALID_ARGUMENT
+    assert run(ctypes.byref(desc(d=96)), ctypes.byref(args()), None) == B.DM_ERR_UNSUPPORTED
+    assert run(ctypes.byref(desc()), ctypes.byref(args(K=9)), None) == B.DM_ERR_INVALID_ARGUMENT
+    # the batched 70B-shaped step: 32 x 8 x 5 fp32 logit rows of 128256 alone are 656 MB
+    big = desc(d=8192, vocab=128256, max_batch=32, gamma=7, k_max=5)
+    assert run(ctypes.byref(big), ctypes.byref(args(B_=32, modes=(B.DM_MODE_JS_MAJORITY,) * 32)),
+               None) == B.DM_ERR_TOO_LARGE
