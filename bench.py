@@ -166,6 +166,33 @@ def cpu_baseline(w, seed, budget_s):
             "single_thread_value": round(rate1, 4), "nproc": nproc, "cpus_available": avail, "cpu_model": model}
 
 
+def graph_replay(torch, step_on, outs, steps, warmup):
+    """One step captured into a HIP graph (every enqueue of the step is a
+    kernel launch), replayed `steps` times after `warmup` replays.  The
+    outputs of the last eager step are kept and compared with those of every
+    replay, with the host synchronising between replays."""
+    eager = {k: v.clone() for k, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_on(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    match = True
+    for _ in range(max(1, warmup)):
+        for v in outs.values():
+            v.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        match = match and all(bool(torch.equal(outs[k], eager[k])) for k in eager)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    match = match and all(bool(torch.equal(outs[k], eager[k])) for k in eager)
+    return {"ms_per_step": round(start.elapsed_time(stop) / steps, 5), "outputs_match": match}
+
+
 def copy_probe(nbytes: int, dev) -> None:
     """One plain device-to-device copy of `nbytes`, for calibrating HBM byte
     counters: rocprofv3's FETCH_SIZE / WRITE_SIZE of this dispatch are
@@ -197,6 +224,9 @@ def main():
     ap.add_argument("--w-layout", choices=("panels", "rowmajor"), default="panels",
                     help="order of the LM-head weight: panels (packed once before timing, as a model loader "
                          "would) or row-major")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step into a HIP graph and time its replays (reported beside the "
+                         "direct launches, which stay the headline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -253,10 +283,13 @@ def main():
             "accept_pos": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=stream.cuda_stream, outputs=outs,
+    def step_on(st):
+        ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=st.cuda_stream, outputs=outs,
                 w_layout=w_layout, temperature=args.temperature, top_k=args.top_k, top_p=args.top_p,
                 tree_parent=tree)
+
+    def step():
+        step_on(stream)
 
     for _ in range(args.warmup):
         step()
@@ -284,6 +317,12 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), median {ms_median * 1e3:.1f}, "
         f"wall {wall / args.steps * 1e6:.1f} us/step; GEMM kernel {gemm_avg * 1e3:.1f} us avg, "
         f"min {min(gemm_ms) * 1e3:.1f} us")
+
+    graph = None
+    if args.graph:
+        graph = graph_replay(torch, step_on, outs, args.steps, args.warmup)
+        log(f"[bench] graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step against {ms_step * 1e3:.1f} direct; "
+            f"outputs identical to the eager step: {graph['outputs_match']}")
 
     positions = cfg.B * (cfg.gamma + 1)
     value = positions / (ms_step / 1e3)
@@ -338,6 +377,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        line["graph_replay"] = graph
     print(json.dumps(line), flush=True)
     ver.close()
 
