@@ -282,6 +282,31 @@ __device__ __forceinline__ int fkey(float x) {
 }
 __device__ __forceinline__ float fkey_inv(int k) { return __int_as_float(k ^ (int)((uint32_t)(k >> 31) >> 1)); }
 
+// 4 x 4 transpose inside each quad of lanes (lanes 4n .. 4n + 3; k = the
+// lane's place in its quad): on entry lane k holds t[j] = element (j, k) of
+// the quad's block, on exit t[i] = element (k, i).  Two butterfly steps:
+// lanes k and k ^ 1 swap the elements whose index differs from k in bit 0,
+// then lanes k and k ^ 2 those differing in bit 1.
+__device__ __forceinline__ void quad_transpose(float (&t)[4], int k) {
+    const bool odd = k & 1, hi = k & 2;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+        const float recv = dpp_f<kDppXor1>(odd ? t[e] : t[e + 1]);
+        if (odd)
+            t[e] = recv;
+        else
+            t[e + 1] = recv;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float recv = dpp_f<kDppXor2>(hi ? t[e] : t[e + 2]);
+        if (hi)
+            t[e] = recv;
+        else
+            t[e + 2] = recv;
+    }
+}
+
 // (max, sum exp, lowest argmax) of J rows, each held as G values per lane by
 // the 16 lanes of a DPP row (lane c holds columns col0 + 16 g); the J
 // reductions are independent, so their DPP steps interleave.
@@ -655,7 +680,9 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 //
 // The epilogue (in the ring's memory): statistics per row and per centroid
 // over each wave's 64 columns, merged across the four panels into
-// part[target][panel group]; stored rows written.
+// part[target][panel group]; stored rows written 16 bytes per lane (a
+// transpose inside each quad of lanes turns the matrix-core output, four
+// rows of one column per lane, into four columns of one row).
 // =====================================================================
 constexpr int kTileWaves = 4;  // 64-column panels per workgroup, one wave each
 
@@ -802,6 +829,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
         // FULL: the panel lies wholly inside the vocabulary (no per-column selects)
         auto epilogue = [&](auto full) __attribute__((always_inline)) {
             constexpr bool FULL = decltype(full)::value;
+            // 16-byte stores of whole quads: a full panel, rows 16-byte aligned
+            const bool vstore = FULL && (P.V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
 #pragma unroll
             for (int m = 0; m < MSUB; ++m) {
                 // the lane group's four rows of sub-tile m: metadata read together,
@@ -817,13 +846,29 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
                         x[j][g] = acc[g][m][j] * mt[j].scale;
                         acc[g][m][j] = x[j][g];
                     }
+                if (vstore) {
+                    // rows kept for the vocabulary pass, 16 bytes per lane: after a
+                    // transpose inside each quad of lanes, lane 16 grp + 4 q + k holds
+                    // columns 16 g + 4 q .. + 3 of row 4 grp + k of the sub-tile
+                    const int k = c16 & 3;
+                    const RowMeta me = s_meta[16 * m + 4 * grp + k];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            if (FULL || ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
+                    for (int g = 0; g < G; ++g) {
+                        float t[4] = {x[0][g], x[1][g], x[2][g], x[3][g]};
+                        quad_transpose(t, k);
+                        if (me.canon >= 0 && me.store)
+                            *(v4f*)(logits + (size_t)me.canon * P.V + my_panel * 64 + 16 * g + 4 * (c16 >> 2)) =
+                                v4f{t[0], t[1], t[2], t[3]};
                     }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
+#pragma unroll
+                            for (int g = 0; g < G; ++g)
+                                if (FULL || ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
+                        }
+                }
                 Stat st[4];
                 row16_stats<4, G, FULL>(x, ok, col0, st);
                 if (c16 == 0) {
