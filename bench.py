@@ -72,15 +72,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm_kernel(cfg, panels: bool, n_lossless: int) -> str:
+def gemm_kernel(cfg, panels: bool, n_lossless: int, lossy_pos=None, lossless_pos=None) -> str:
     """Which LM-head kernel the library launches: row-major W takes
     k_gemm_skinny; panel-order W takes k_gemm_panel when the rows fit one
     small tile (4 lane groups of 4 * ms slots, ms = 1..4, a position's K heads
-    in one group) and k_gemm_tile otherwise."""
+    in one group) and k_gemm_tile otherwise.  The live position counts of a
+    ragged batch may be given (default: gamma + 1 per sequence)."""
     if not panels:
         return "k_gemm_skinny"
     T1 = cfg.gamma + 1
-    lossy_pos, lossless_pos = (cfg.B - n_lossless) * T1, n_lossless * T1
+    if lossy_pos is None:
+        lossy_pos, lossless_pos = (cfg.B - n_lossless) * T1, n_lossless * T1
     best = None
     for ms in range(1, 5):
         S = 4 * ms
@@ -224,6 +226,9 @@ def main():
     ap.add_argument("--w-layout", choices=("panels", "rowmajor"), default="panels",
                     help="order of the LM-head weight: panels (packed once before timing, as a model loader "
                          "would) or row-major")
+    ap.add_argument("--ragged", type=int, default=0,
+                    help="a ragged batch: each sequence's draft count drawn uniformly from 0..gamma with this "
+                         "seed (0 = every sequence drafts gamma)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step into a HIP graph and time its replays (reported beside the "
                          "direct launches, which stay the headline)")
@@ -283,10 +288,14 @@ def main():
             "accept_pos": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream(dev)
 
+    seq_gamma = None
+    if args.ragged:
+        seq_gamma = np.random.default_rng(args.ragged).integers(0, cfg.gamma + 1, cfg.B).astype(np.int32)
+
     def step_on(st):
         ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=st.cuda_stream, outputs=outs,
                 w_layout=w_layout, temperature=args.temperature, top_k=args.top_k, top_p=args.top_p,
-                tree_parent=tree)
+                tree_parent=tree, seq_gamma=seq_gamma)
 
     def step():
         step_on(stream)
@@ -324,10 +333,12 @@ def main():
         log(f"[bench] graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step against {ms_step * 1e3:.1f} direct; "
             f"outputs identical to the eager step: {graph['outputs_match']}")
 
-    positions = cfg.B * (cfg.gamma + 1)
-    value = positions / (ms_step / 1e3)
     n_lossless = int((w.modes == wl.LOSSLESS).sum())
-    rows = (cfg.B - n_lossless) * (cfg.gamma + 1) * cfg.K + n_lossless * (cfg.gamma + 1)
+    per_seq = (seq_gamma + 1) if seq_gamma is not None else np.full(cfg.B, cfg.gamma + 1)
+    lossless_seq = w.modes == wl.LOSSLESS
+    positions = int(per_seq.sum())
+    value = positions / (ms_step / 1e3)
+    rows = int(per_seq[~lossless_seq].sum()) * cfg.K + int(per_seq[lossless_seq].sum())
     elem = 2 if cfg.dtype == wl.DTYPE_BF16 else 4
     alg_bytes = cfg.V * cfg.d * elem + positions * cfg.d * elem
     alg_flops = 2.0 * rows * cfg.d * cfg.V
@@ -343,8 +354,10 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dname]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-    roof["kernel"] = gemm_kernel(cfg, w_layout == Bd.DM_W_PANELS, n_lossless)
-    roof["traffic"] = measured_traffic(cfg.name, roof["kernel"])
+    roof["kernel"] = gemm_kernel(cfg, w_layout == Bd.DM_W_PANELS, n_lossless, int(per_seq[~lossless_seq].sum()),
+                                 int(per_seq[lossless_seq].sum()))
+    # the committed counter records cover the full (non-ragged) workloads only
+    roof["traffic"] = None if seq_gamma is not None else measured_traffic(cfg.name, roof["kernel"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -373,6 +386,7 @@ def main():
         "config": {"workload": f"{cfg.name}: B={cfg.B}, gamma={cfg.gamma}, d={cfg.d}, |V|={cfg.V}, K={cfg.K}, "
                                f"p_drop={cfg.p_drop}, {modes_desc}",
                    "batch": cfg.B, "positions_per_step": positions, "gemm_rows": rows, "w_layout": args.w_layout,
+                   "ragged_seed": args.ragged or None,
                    "sampling": {"temperature": args.temperature, "top_k": args.top_k, "top_p": args.top_p}},
         "roofline": roof,
         "cpu_baseline": cpu,

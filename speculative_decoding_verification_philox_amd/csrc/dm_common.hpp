@@ -55,6 +55,12 @@ struct Plan {
     uint8_t seq_gamma[kMaxBatch], seq_k[kMaxBatch], seq_pi[kMaxBatch];
     uint32_t p_thresh[kMaxDropValues];
     float p_scale[kMaxDropValues];
+    // ragged batches lay out live positions only: class 0 (lossy) and 1
+    // (lossless) number their positions sequence by sequence in batch
+    // order; rk_seq[c][r] is the r-th sequence of class c and rk_start[c][r]
+    // its first position (rk_start[c][n] the class's position count)
+    uint8_t rk_seq[2][kMaxBatch];
+    uint16_t rk_start[2][kMaxBatch + 1];
     // slot layout
     int geom, msub, MT, GR, S;
     int ppg;                // lossy positions per group (S / K)
@@ -170,6 +176,28 @@ struct RowInfo {
     int lossy_pos; // index of the lossy position (centroid slot), -1 otherwise
 };
 
+// Sequence b and position t of live position p of class cls (0 lossy, 1
+// lossless).  A uniform batch has gamma + 1 positions per sequence; a ragged
+// one gamma_b + 1, found by a binary search of the class's starts.
+__host__ __device__ inline void class_pos(const Plan& P, int cls, int p, int* b, int* t) {
+    if (!P.ragged) {
+        *b = select_of(P.lossless_bits, P.B, p / P.T1, cls == 1);
+        *t = p % P.T1;
+        return;
+    }
+    const uint16_t* start = P.rk_start[cls];
+    int lo = 0, hi = (cls ? P.n_lossless_seq : P.n_lossy_seq) - 1;  // the last r with start[r] <= p
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)start[mid] <= p)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    *b = P.rk_seq[cls][lo];
+    *t = p - (int)start[lo];
+}
+
 __host__ __device__ inline RowInfo row_info(const Plan& P, int rho) {
     RowInfo ri{-1, 0, 0, 0, -1};
     int tile = rho / P.MT, r = rho - tile * P.MT;
@@ -180,21 +208,18 @@ __host__ __device__ inline RowInfo row_info(const Plan& P, int rho) {
         if (slot >= P.ppg) return ri;
         int p = (tile * P.GR + g) * P.ppg + slot;
         if (p >= P.n_lossy_pos) return ri;
-        ri.b = select_of(P.lossless_bits, P.B, p / P.T1, false);
-        ri.t = p % P.T1;
+        class_pos(P, 0, p, &ri.b, &ri.t);
         ri.i = lam - slot * P.K;
         ri.lossy = 1;
         ri.lossy_pos = p;
-        // a ragged sequence's rows past its drafts or heads are padding
-        if (P.ragged && (ri.t > P.seq_gamma[ri.b] || ri.i >= P.seq_k[ri.b])) return RowInfo{-1, 0, 0, 0, -1};
+        // a ragged sequence's head slots past its heads are padding
+        if (P.ragged && ri.i >= P.seq_k[ri.b]) return RowInfo{-1, 0, 0, 0, -1};
     } else {
         int q = ((tile - P.tiles_lossy) * P.GR + g) * P.S + lam;
         if (q >= P.n_lossless_pos) return ri;
-        ri.b = select_of(P.lossless_bits, P.B, q / P.T1, true);
-        ri.t = q % P.T1;
+        class_pos(P, 1, q, &ri.b, &ri.t);
         ri.i = 0;
         ri.lossy = 0;
-        if (P.ragged && ri.t > P.seq_gamma[ri.b]) return RowInfo{-1, 0, 0, 0, -1};
     }
     return ri;
 }

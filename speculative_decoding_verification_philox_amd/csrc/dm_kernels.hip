@@ -205,7 +205,9 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ W, u
 // all K slots in head order equals the sum over the K_b heads.
 __device__ __forceinline__ float lossy_pos_inv_k(const Plan& P, int p) {
     if (!P.ragged || p >= P.n_lossy_pos) return P.inv_k;
-    return seq_inv_k(P, select_of(P.lossless_bits, P.B, p / P.T1, false));
+    int b, t;
+    class_pos(P, 0, p, &b, &t);
+    return seq_inv_k(P, b);
 }
 
 // =====================================================================
@@ -1180,10 +1182,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
         head = ri.i;
         lossless = !ri.lossy;
     } else {
-        const int p = t - P.R_phys;
-        b = select_of(P.lossless_bits, P.B, p / P.T1, false);
-        pos_t = p % P.T1;
-        if (pos_t > seq_G(P, b)) return;  // past a ragged sequence's drafts: the whole block leaves
+        class_pos(P, 0, t - P.R_phys, &b, &pos_t);
     }
     const Stat* src = part + (size_t)t * P.n_vgroups;
     Stat st = stat_empty();

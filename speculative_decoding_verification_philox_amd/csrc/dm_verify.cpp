@@ -113,8 +113,11 @@ uint32_t drop_threshold(float p_drop) {
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Row layout and work split of one call.
-void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, int w_packed, Plan& P) {
+// Row layout and work split of one call.  lossy_pos / lossless_pos are the
+// live positions of each class (a ragged batch has fewer than gamma + 1 per
+// sequence); -1 means gamma + 1 per sequence.
+void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, int w_packed, Plan& P,
+               int lossy_pos = -1, int lossless_pos = -1) {
     // counts only; the sequence bit sets are filled in by the caller
     P.B = B;
     P.T1 = D.gamma + 1;
@@ -126,8 +129,8 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
     P.n_lossless_seq = n_lossless;
     P.n_lossy_seq = B - n_lossless;
     P.n_js_seq = n_js;
-    P.n_lossy_pos = P.n_lossy_seq * P.T1;
-    P.n_lossless_pos = n_lossless * P.T1;
+    P.n_lossy_pos = lossy_pos >= 0 ? lossy_pos : P.n_lossy_seq * P.T1;
+    P.n_lossless_pos = lossless_pos >= 0 ? lossless_pos : n_lossless * P.T1;
 
     // smallest number of tiles, then the fewest rows
     P.geom = 0;
@@ -309,11 +312,14 @@ Workspace carve(uint8_t* base, const Sizes& s) {
 // sequence sets, scales, thresholds and the Philox key.
 void plan_call(const dm_verify_desc& D, const dm_verify_args* a, Plan& P) {
     int n_lossless = 0, n_js = 0;
+    // live positions of each class: a ragged sequence verifies gamma_b + 1
+    int live[2] = {0, 0};
     for (int b = 0; b < a->batch; ++b) {
         n_lossless += a->modes[b] == DM_MODE_LOSSLESS;
         n_js += a->modes[b] == DM_MODE_JS_MAJORITY;
+        live[a->modes[b] == DM_MODE_LOSSLESS] += (a->seq_gamma ? a->seq_gamma[b] : D.gamma) + 1;
     }
-    make_plan(D, a->batch, a->K, n_lossless, n_js, (int)a->w_layout, P);
+    make_plan(D, a->batch, a->K, n_lossless, n_js, (int)a->w_layout, P, live[0], live[1]);
     for (int b = 0; b < a->batch; ++b) {
         if (a->modes[b] == DM_MODE_LOSSLESS) P.lossless_bits[b >> 5] |= 1u << (b & 31);
         if (a->modes[b] == DM_MODE_JS_MAJORITY) P.js_bits[b >> 5] |= 1u << (b & 31);
@@ -342,6 +348,13 @@ void plan_call(const dm_verify_desc& D, const dm_verify_args* a, Plan& P) {
                 P.p_scale[k] = (float)(1.0 / ((1.0 - (double)pb) * temp));
             }
             P.seq_pi[b] = (uint8_t)k;
+        }
+        int rank[2] = {0, 0};
+        for (int b = 0; b < a->batch; ++b) {
+            const int c = a->modes[b] == DM_MODE_LOSSLESS;
+            P.rk_seq[c][rank[c]] = (uint8_t)b;
+            P.rk_start[c][rank[c] + 1] = (uint16_t)(P.rk_start[c][rank[c]] + P.seq_gamma[b] + 1);
+            ++rank[c];
         }
     }
     P.filter = n_lossless > 0 && ((a->top_k > 0 && a->top_k < D.vocab) || (a->top_p > 0.0f && a->top_p < 1.0f));

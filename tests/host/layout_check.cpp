@@ -123,6 +123,88 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
     }
 }
 
+// Ragged batches (per-sequence drafts and heads) through plan_call: only
+// live positions get rows, every live (b, t, i) exactly once, a position's
+// heads in one lane group, and class_pos inverting the position numbering.
+static void check_ragged_case(int d, int V, int maxB, int gamma, int kmax, int B, int K, unsigned seed, int wp) {
+    dm_verify_desc D{d, V, maxB, gamma, kmax, DM_DTYPE_BF16};
+    std::vector<uint8_t> modes(B);
+    std::vector<int32_t> sg(B), sk(B);
+    unsigned s = seed * 2654435761u + 1u;
+    for (int b = 0; b < B; ++b) {
+        s = s * 1103515245u + 12345u;
+        modes[b] = (uint8_t)((s >> 16) % 4);
+        s = s * 1103515245u + 12345u;
+        sg[b] = (int)((s >> 16) % (unsigned)(gamma + 1));
+        s = s * 1103515245u + 12345u;
+        sk[b] = 1 + (int)((s >> 16) % (unsigned)K);
+    }
+    dm_verify_args a{};
+    a.modes = modes.data();
+    a.batch = B;
+    a.K = K;
+    a.p_drop = 0.2f;
+    a.w_layout = (uint32_t)wp;
+    a.seq_gamma = sg.data();
+    a.seq_heads = sk.data();
+    Plan P{};
+    plan_call(D, &a, P);
+    const int T1 = gamma + 1;
+    int live[2] = {0, 0};
+    for (int b = 0; b < B; ++b) live[modes[b] == DM_MODE_LOSSLESS] += sg[b] + 1;
+    CHECK(P.ragged && P.n_lossy_pos == live[0] && P.n_lossless_pos == live[1], "ragged position counts\n");
+    Sizes sz = workspace_sizes(D);
+    CHECK((size_t)P.R_phys * d * 2 <= sz.hm && (size_t)P.R_phys * sizeof(RowMeta) <= sz.meta, "ragged Hm\n");
+    CHECK((size_t)P.n_vgroups * (P.R_phys + P.n_lossy_pos) * sizeof(Stat) <= sz.part, "ragged part\n");
+    std::vector<int> seen((size_t)B * T1 * K, 0);
+    int rows_live = 0;
+    for (int rho = 0; rho < P.R_phys; ++rho) {
+        RowInfo ri = row_info(P, rho);
+        if (ri.b < 0) continue;
+        ++rows_live;
+        CHECK(ri.b < B && ri.t >= 0 && ri.t <= sg[ri.b] && ri.i >= 0, "ragged row %d out of range\n", rho);
+        const bool lossless = modes[ri.b] == DM_MODE_LOSSLESS;
+        CHECK(lossless ? ri.i == 0 : ri.i < sk[ri.b], "ragged row %d head\n", rho);
+        if (ri.b < B && ri.t >= 0 && ri.t < T1 && ri.i >= 0 && ri.i < K) seen[((size_t)ri.b * T1 + ri.t) * K + ri.i]++;
+    }
+    int want_rows = 0;
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t <= sg[b]; ++t) {
+            const int heads = modes[b] == DM_MODE_LOSSLESS ? 1 : sk[b];
+            want_rows += heads;
+            for (int i = 0; i < heads; ++i)
+                CHECK(seen[((size_t)b * T1 + t) * K + i] == 1, "ragged coverage b=%d t=%d i=%d\n", b, t, i);
+        }
+    CHECK(rows_live == want_rows, "ragged live rows %d, want %d\n", rows_live, want_rows);
+    // rows computed: the tiles the live positions need, no more
+    const int tiles = (live[0] ? (live[0] + P.GR * P.ppg - 1) / (P.GR * P.ppg) : 0) +
+                      (live[1] ? (live[1] + P.GR * P.S - 1) / (P.GR * P.S) : 0);
+    CHECK(P.n_tiles == tiles && P.R_phys == tiles * P.MT, "ragged tiles %d, want %d\n", P.n_tiles, tiles);
+    for (int c = 0; c < 2; ++c) {
+        const int n = c ? P.n_lossless_pos : P.n_lossy_pos;
+        int pb = -1, pt = -1;
+        for (int p = 0; p < n; ++p) {
+            int b, t;
+            class_pos(P, c, p, &b, &t);
+            CHECK(b >= 0 && b < B && (modes[b] == DM_MODE_LOSSLESS) == (c == 1) && t >= 0 && t <= sg[b],
+                  "class_pos %d %d\n", c, p);
+            CHECK(b > pb || (b == pb && t == pt + 1), "class_pos order %d %d\n", c, p);
+            pb = b;
+            pt = t;
+        }
+    }
+    for (int p = 0; p < P.n_lossy_pos; ++p) {
+        int r0 = lossy_row(P, p, 0);
+        for (int i = 1; i < K; ++i) {
+            int r = lossy_row(P, p, i);
+            int g0, l0, g1, l1;
+            tile_slot(P.geom, r0 % P.MT, &g0, &l0);
+            tile_slot(P.geom, r % P.MT, &g1, &l1);
+            CHECK(r / P.MT == r0 / P.MT && g0 == g1 && l1 == l0 + i, "ragged position %d heads split\n", p);
+        }
+    }
+}
+
 // select_of against a plain scan, for random sets and every rank.
 static void check_select() {
     unsigned s = 12345u;
@@ -174,6 +256,14 @@ int main() {
         check_case(4096, 128256, 1, 7, 5, 1, 5, 0, wp);
         cases += 3;
     }
+    for (int wp = 0; wp <= 1; ++wp)
+        for (int K : {1, 3, 5, 8, 16})
+            for (int B : {1, 5, 32, 64, 256})
+                for (int gamma : {0, 3, 7, 63})
+                    for (unsigned seed : {0u, 1u, 2u}) {
+                        check_ragged_case(512, 5003, 256, gamma, 16, B, K, seed, wp);
+                        ++cases;
+                    }
     std::printf("%d cases, %d failures\n", cases, fails);
     return fails ? 1 : 0;
 }
