@@ -166,7 +166,7 @@ struct RowMeta {
     int canon;    // (b * T1 + t) * K + i, or -1 for a padding row
     float scale;  // 1 / ((1 - p_drop) T) for a dropout row, 1 / T undropped, 0 padding
     int store;    // 1 if the row's logits are kept for the vocabulary pass
-    int pad;
+    float inv_k;  // 1 / K_b of a dropout row's sequence (its position's centroid weight), 0 otherwise
 };
 
 // What a physical GEMM row holds.

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
         mt.scale = valid ? (ri.lossy ? seq_scale(P, ri.b) : P.scale_undropped) : 0.0f;
         mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < seq_G(P, ri.b)));
-        mt.pad = 0;
+        mt.inv_k = valid && ri.lossy ? seq_inv_k(P, ri.b) : 0.0f;
         meta[rho] = mt;
     }
     // this thread: elements 8 e .. 8 e + 7 of the row
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
         mt.scale = valid ? (ri.lossy ? seq_scale(P, ri.b) : P.scale_undropped) : 0.0f;
         mt.store = valid && (P.store_all || !ri.lossy || (bit_of(P.js_bits, ri.b) && ri.t < seq_G(P, ri.b)));
-        mt.pad = 0;
+        mt.inv_k = valid && ri.lossy ? seq_inv_k(P, ri.b) : 0.0f;
         meta[rho] = mt;
     }
     uint32_t bits = 0u;  // bit k: keep element e0 + k
@@ -387,8 +387,9 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
 // slot advance with lam, i wrapping at K; both uniform).  The head rows are
 // summed in head order as they go by (the order every kernel uses for the
 // centroid, see centroid_logit) and the position's statistics are taken at
-// its last head.  ACC(lam, g) yields the scaled row value of slot lam.
-#define DM_CENTROID_PASS(NSLOT, ACC, pos_base, write, dst)                          \
+// its last head.  ACC(lam, g) yields the scaled row value of slot lam and
+// INVW(p) the centroid weight (1 / K_b) of the lane group's p-th position.
+#define DM_CENTROID_PASS(NSLOT, ACC, INVW, write, dst)                          \
     do {                                                                            \
         float csum_[G];                                                             \
         int i_ = 0, slot_ = 0;                                                      \
@@ -400,7 +401,7 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
             }                                                                       \
             if (i_ == P.K - 1) {                                                    \
                 if (slot_ < P.ppg) {                                                \
-                    const float inv_ = lossy_pos_inv_k(P, (pos_base) + slot_);      \
+                    const float inv_ = INVW(slot_);                              \
                     float xc_[1][G];                                                \
                     _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) xc_[0][g_] = csum_[g_] * inv_; \
                     Stat st_[1];                                                    \
@@ -420,13 +421,13 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
 // statistics of all NSLOT / KC positions of the lane group are reduced
 // together, so their DPP steps interleave instead of running one position
 // after another.
-#define DM_CENTROID_K(KC, NSLOT, ACC, pos_base, write, dst)                        \
+#define DM_CENTROID_K(KC, NSLOT, ACC, INVW, write, dst)                        \
     do {                                                                           \
         constexpr int NP_ = (NSLOT) / (KC);                                        \
         if constexpr (NP_ > 0) {                                                   \
             float xc_[NP_ > 0 ? NP_ : 1][G];                                       \
             _Pragma("unroll") for (int p_ = 0; p_ < NP_; ++p_) {                    \
-                const float inv_ = lossy_pos_inv_k(P, (pos_base) + p_);             \
+                const float inv_ = INVW(p_);                                     \
                 _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) {                 \
                     float s_ = ACC(p_ * (KC), g_);                                  \
                     _Pragma("unroll") for (int i_ = 1; i_ < (KC); ++i_) s_ += ACC(p_ * (KC) + i_, g_); \
@@ -443,14 +444,14 @@ __device__ __forceinline__ void row16_stats(const float (&x)[J][G], const bool (
 
 // Centroid statistics of a lane group: the common head counts take the
 // interleaved pass on full panels, every other case the running one.
-#define DM_CENTROIDS(NSLOT, ACC, pos_base, write, dst)                             \
+#define DM_CENTROIDS(NSLOT, ACC, INVW, write, dst)                             \
     do {                                                                           \
         if (FULL && P.K == 5)                                                      \
-            DM_CENTROID_K(5, NSLOT, ACC, pos_base, write, dst);                     \
+            DM_CENTROID_K(5, NSLOT, ACC, INVW, write, dst);                     \
         else if (FULL && P.K == 8)                                                 \
-            DM_CENTROID_K(8, NSLOT, ACC, pos_base, write, dst);                     \
+            DM_CENTROID_K(8, NSLOT, ACC, INVW, write, dst);                     \
         else                                                                       \
-            DM_CENTROID_PASS(NSLOT, ACC, pos_base, write, dst);                    \
+            DM_CENTROID_PASS(NSLOT, ACC, INVW, write, dst);                    \
     } while (0)
 
 template <bool BF16, int MSUB, bool DEEP>
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
     const int nkb = P.nkb;
 
     // metadata of tile row `lane`, fetched now, read through shuffles later
-    RowMeta my = RowMeta{-1, 0.0f, 0, 0};
+    RowMeta my = RowMeta{-1, 0.0f, 0, 0.0f};
     if (lane < ROWS) my = meta[(size_t)tile * ROWS + lane];
 
     v4f acc[G][MSUB];
@@ -626,7 +627,10 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
         }
         if (lossy_tile) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-            DM_CENTROIDS(4 * MSUB, DM_ACC, tile * npt + grp * P.ppg, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
+            // a ragged batch's weight sits in the metadata of the position's first head row
+#define DM_INVW(p) (P.ragged ? __shfl(my.inv_k, 16 * (((p) * P.K) >> 2) + 4 * grp + (((p) * P.K) & 3), 64) : P.inv_k)
+            DM_CENTROIDS(4 * MSUB, DM_ACC, DM_INVW, c == 0, &s_st[wave][ROWS + grp * P.ppg]);
+#undef DM_INVW
 #undef DM_ACC
         }
     };
@@ -880,8 +884,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
             }
             if (tile < P.tiles_lossy) {
 #define DM_ACC(lam, g) acc[g][(lam) >> 2][(lam) & 3]
-                DM_CENTROIDS(4 * MSUB, DM_ACC, tile * (P.GR * P.ppg) + grp * P.ppg, c16 == 0,
-                             &my_st[ROWS + grp * P.ppg]);
+                // a ragged batch's weight sits in the metadata of the position's first head row
+#define DM_INVW(p) (P.ragged ? s_meta[16 * (((p) * P.K) >> 2) + 4 * grp + (((p) * P.K) & 3)].inv_k : P.inv_k)
+                DM_CENTROIDS(4 * MSUB, DM_ACC, DM_INVW, c16 == 0, &my_st[ROWS + grp * P.ppg]);
+#undef DM_INVW
 #undef DM_ACC
             }
         };
@@ -1122,8 +1128,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
         const int p = tile * npt + lane;
         Stat st = stat_empty();
         if (p < P.n_lossy_pos) {
+            const float inv_k = lossy_pos_inv_k(P, p);
             for (int c = 0; c < ncol; ++c) {
-                float lb = centroid_logit(P.K, lossy_pos_inv_k(P, p),
+                float lb = centroid_logit(P.K, inv_k,
                                           [&](int i) { return et[tile_row(0, g, slot * P.K + i) * PITCH + c]; });
                 stat_push(st, lb, vbase + c);
             }
