@@ -1,5 +1,6 @@
 """GPU parity at the workloads' full sizes (the five chain workloads and the
-token tree at the 70B head), over Philox seeds 1..20.
+token tree at the 70B head), over Philox seeds 1..20, and a ragged batch of
+the batched 70B over seeds 1..4.
 
 For every seed the library runs on the same inputs exactly as bench.py times
 it (panel-order W, no inspection outputs) and once more with every
@@ -36,7 +37,7 @@ def window(B, per_seed):
     return lambda seed: [(seed * per_seed + k) % B for k in range(per_seed)]
 
 
-def _full(cfg_index, per_seed=1, p_values=None, seeds=SEEDS):
+def _full(cfg_index, per_seed=1, p_values=None, seeds=SEEDS, ragged=None):
     w = wl.generate(cfg_index)
     cfg = w.cfg
     print(f"  {cfg.name}: B={cfg.B} d={cfg.d} V={cfg.V} K={cfg.K}", flush=True)
@@ -50,17 +51,19 @@ def _full(cfg_index, per_seed=1, p_values=None, seeds=SEEDS):
             seqs = pick(seed)
             covered.update(seqs)
             print(f"  p_drop={p} seed={seed} oracle sequences={seqs}", flush=True)
-            o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs, tree=w.tree_parent)
+            o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, w.modes, cfg.K, p, seed, seqs=seqs, tree=w.tree_parent,
+                             ragged=ragged)
             g_bench = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=P.PANELS,
-                                tree=w.tree_parent)
-            g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=P.PANELS, tree=w.tree_parent)
+                                tree=w.tree_parent, ragged=ragged)
+            g_dbg = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=True, layout=P.PANELS, tree=w.tree_parent,
+                              ragged=ragged)
             g_row = P.run_gpu(ver, inp, w.modes, cfg.K, p, seed, debug=False, layout=P.ROW_MAJOR,
-                              tree=w.tree_parent)
+                              tree=w.tree_parent, ragged=ragged)
             for k in ("accept_len", "accept_pos", "out_token"):
                 np.testing.assert_array_equal(g_bench[k], g_dbg[k], err_msg=k)
-            rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs))
-            rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
-            rep.add(P.compare(g_row, o, w.modes, cfg.K, seqs=seqs, check_debug=False))
+            rep.add(P.compare(g_dbg, o, w.modes, cfg.K, seqs=seqs, ragged=ragged))
+            rep.add(P.compare(g_bench, o, w.modes, cfg.K, seqs=seqs, check_debug=False, ragged=ragged))
+            rep.add(P.compare(g_row, o, w.modes, cfg.K, seqs=seqs, check_debug=False, ragged=ragged))
     ver.close()
     assert covered == set(range(cfg.B)), f"sequences never compared: {sorted(set(range(cfg.B)) - covered)}"
     P.assert_caps(rep, f"({cfg.name})")
@@ -79,6 +82,15 @@ def test_config2_llama31_70b_head_pdrop_sweep(p_drop):
 def test_config3_batched_70b():
     # 2 sequences per seed: 40 over the 20 seeds, all 32 covered
     _full(3, per_seed=2)
+
+
+def test_config3_batched_70b_ragged():
+    """The ragged batch bench.py --ragged 7 times: each sequence's draft
+    count drawn from 0..gamma with generator seed 7 (153 of 256 positions
+    live, five 160-row tiles), on a window of 8 sequences per seed."""
+    cfg = wl.CONFIGS[3]
+    seq_gamma = np.random.default_rng(7).integers(0, cfg.gamma + 1, cfg.B).astype(np.int32)
+    _full(3, per_seed=8, seeds=range(1, 5), ragged=dict(seq_gamma=seq_gamma))
 
 
 def test_config4_wide_mixed():
