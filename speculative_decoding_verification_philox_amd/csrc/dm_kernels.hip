@@ -832,11 +832,17 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
         bool ok[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) ok[g] = my_panel < P.n_panels && col0 + 16 * g < P.V;
-        // FULL: the panel lies wholly inside the vocabulary (no per-column selects)
-        auto epilogue = [&](auto full) __attribute__((always_inline)) {
-            constexpr bool FULL = decltype(full)::value;
-            // 16-byte stores of whole quads: a full panel, rows 16-byte aligned
-            const bool vstore = FULL && (P.V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+        // One epilogue for every real panel, free of per-column tests (a second,
+        // tested copy would cost this one its registers).  The one panel the
+        // vocabulary cuts (`cut`, a uniform branch no other wave takes) sets
+        // its columns past the vocabulary to -inf, which the statistics and
+        // the centroid sums ignore, and stores none of them.
+        if (my_panel < P.n_panels) {
+            constexpr bool FULL = true;
+            const bool cut = (my_panel + 1) * 64 > P.V;
+            // 16-byte stores of whole quads: rows 16-byte aligned (V % 4 == 0,
+            // so a quad's four columns are all inside or all past the vocabulary)
+            const bool vstore = (P.V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
 #pragma unroll
             for (int m = 0; m < MSUB; ++m) {
                 // the lane group's four rows of sub-tile m: metadata read together,
@@ -848,10 +854,17 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        x[j][g] = acc[g][m][j] * mt[j].scale;
-                        acc[g][m][j] = x[j][g];
-                    }
+                    for (int g = 0; g < G; ++g) x[j][g] = acc[g][m][j] * mt[j].scale;
+                if (cut) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int g = 0; g < G; ++g) x[j][g] = ok[g] ? x[j][g] : -INFINITY;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) acc[g][m][j] = x[j][g];
                 if (vstore) {
                     // rows kept for the vocabulary pass, 16 bytes per lane: after a
                     // transpose inside each quad of lanes, lane 16 grp + 4 q + k holds
@@ -862,7 +875,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
                     for (int g = 0; g < G; ++g) {
                         float t[4] = {x[0][g], x[1][g], x[2][g], x[3][g]};
                         quad_transpose(t, k);
-                        if (me.canon >= 0 && me.store)
+                        if (me.canon >= 0 && me.store && (!cut || my_panel * 64 + 16 * g + 4 * (c16 >> 2) < P.V))
                             *(v4f*)(logits + (size_t)me.canon * P.V + my_panel * 64 + 16 * g + 4 * (c16 >> 2)) =
                                 v4f{t[0], t[1], t[2], t[3]};
                     }
@@ -872,7 +885,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
                         if (mt[j].canon >= 0 && mt[j].store) {  // the whole 16-lane row agrees
 #pragma unroll
                             for (int g = 0; g < G; ++g)
-                                if (FULL || ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
+                                if (!cut || ok[g]) logits[(size_t)mt[j].canon * P.V + col0 + 16 * g] = x[j][g];
                         }
                 }
                 Stat st[4];
@@ -890,11 +903,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
 #undef DM_INVW
 #undef DM_ACC
             }
-        };
-        if (my_panel < P.n_panels && (my_panel + 1) * 64 <= P.V)
-            epilogue(BoolTag<true>{});
-        else
-            epilogue(BoolTag<false>{});
+        } else {
+            // a panel past the last one: no columns, empty statistics for the merge
+            for (int t = lane; t < 2 * ROWS; t += 64) my_st[t] = stat_empty();
+        }
     }
     __syncthreads();
     // merge the four panels in panel order: part[target][panel group]
@@ -2098,7 +2110,9 @@ static hipError_t launch_tile_t(const Plan& P, const void* Wp, const void* Hp, c
         case 7: hipLaunchKernelGGL((k_gemm_tile<BF16, 7>), grid, block, 0, st, P, w, a, meta, logits, part); break;
         case 8: hipLaunchKernelGGL((k_gemm_tile<BF16, 8>), grid, block, 0, st, P, w, a, meta, logits, part); break;
         case 9: hipLaunchKernelGGL((k_gemm_tile<BF16, 9>), grid, block, 0, st, P, w, a, meta, logits, part); break;
-        case 10: hipLaunchKernelGGL((k_gemm_tile<BF16, 10>), grid, block, 0, st, P, w, a, meta, logits, part); break;
+        case 10:
+            hipLaunchKernelGGL((k_gemm_tile<BF16, 10>), grid, block, 0, st, P, w, a, meta, logits, part);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

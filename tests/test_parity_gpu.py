@@ -359,6 +359,27 @@ def test_tile_kernel_every_sub_tile_count(B, gamma, K, V):
         _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.3, [7], layout=P.PANELS)
 
 
+# vocabularies of whole 64-column panels: the tile kernel's instance without
+# per-column tests; 1152 = 18 panels, so the last group of four holds two
+# panels past the vocabulary, 1024 = 16 panels in four whole groups
+WHOLE_PANEL_CASES = [(1, 12, 15, 1152), (3, 10, 15, 1152), (2, 8, 14, 1024), (5, 4, 11, 1152), (5, 4, 13, 1152),
+                     (7, 6, 10, 1024)]
+
+
+@pytest.mark.parametrize("B,gamma,K,V", WHOLE_PANEL_CASES,
+                         ids=[f"B{b}g{g}K{k}V{v}" for b, g, k, v in WHOLE_PANEL_CASES])
+def test_tile_kernel_whole_panels(B, gamma, K, V):
+    """The tile kernel when the vocabulary ends on a panel boundary (as at
+    |V| = 128256 and 151936), with and without panels past the last one in
+    the final workgroup, on JS and on mixed rules."""
+    assert V % 64 == 0
+    print(f"  tile plan (sub-tiles, tiles) = {_tile_choice(B * (gamma + 1), K)}", flush=True)
+    w = wl.generate(1, B=B, gamma=gamma, d=320, V=V, K=K, planted=0.8)
+    _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, [2], layout=P.PANELS)
+    modes = np.arange(B, dtype=np.uint8) % 3
+    _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.3, [5], layout=P.PANELS)
+
+
 def test_tile_kernel_four_sub_tiles_mixed_rules():
     """One JS and one lossless sequence of eight positions at K = 5: each
     rule's rows fill one 64-row tile, so the tile kernel runs with four
