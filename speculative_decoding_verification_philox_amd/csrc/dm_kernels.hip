@@ -736,7 +736,9 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
     constexpr size_t ST_BYTES = (size_t)kTileWaves * 2 * ROWS * sizeof(Stat);
     __shared__ __align__(16) uint8_t ring[TS::LDS];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform: in scalar registers, so are the panel and
+    // every load offset derived from it
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n_groups = (P.n_panels + 3) >> 2;
     const int per_xcd = (n_groups + 7) >> 3;
     const int xcd = blockIdx.x & 7, k_local = blockIdx.x >> 3;
