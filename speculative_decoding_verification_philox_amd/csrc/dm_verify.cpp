@@ -37,8 +37,11 @@ namespace {
 
 constexpr int kGroupsPerTile = 4;
 // Planner weight of one tile of the matrix-core kernel, in rows: every tile
-// streams the whole weight slice of its panel group.
-constexpr double kTileFixedRows = 256.0;
+// streams the whole weight slice of its panel group and runs one epilogue.
+// Fitted to GEMM times over every sub-tile count at the wide mixed shape
+// (1728 rows, K = 8; the fit gives 24..51 rows per tile) and checked at the
+// batched 70B and the 60-node tree, whose best counts it keeps.
+constexpr double kTileFixedRows = 40.0;
 // The vocabulary pass splits a position into at most 256 chunks of 2048.
 constexpr int kMaxVocab = 256 * 2048;  // 16x16 MFMA output: four row groups per lane
 

@@ -317,7 +317,7 @@ def _tile_choice(n_pos, K, n_lossless=0):
     groups of (4 * sub-tiles) // K positions per tile) and n_lossless
     lossless positions (one row each, in tiles of their own): 64-row tiles
     first; past one of those, the tile kernel with 4..10 sub-tiles, the
-    fewest tiles x (rows per tile + 256), ties to the larger tile.  Used only
+    fewest tiles x (rows per tile + 40), ties to the larger tile.  Used only
     to choose and label the cases below."""
     def tiles(ms):
         tl = -(-n_pos // (4 * ((4 * ms) // K))) if n_pos else 0
@@ -325,7 +325,7 @@ def _tile_choice(n_pos, K, n_lossless=0):
     small = min(tiles(ms) for ms in range(1, 5) if 4 * ms >= K or not n_pos)
     if small <= 1:
         return None
-    ms = min(range(4, 11), key=lambda ms: (tiles(ms) * (16 * ms + 256), -ms))
+    ms = min(range(4, 11), key=lambda ms: (tiles(ms) * (16 * ms + 40), -ms))
     return ms, tiles(ms)
 
 
@@ -333,7 +333,7 @@ def _tile_choice(n_pos, K, n_lossless=0):
 # the mixed-rule test below), at one to five tiles.  |V| = 1000 leaves four
 # panel groups (the last panel 40 columns wide), so four of the eight XCD
 # slots idle; |V| = 2100 leaves a ninth group holding one 52-column panel.
-TILE_CASES = [(1, 4, 9, 1000), (1, 12, 11, 2100), (2, 8, 14, 1000), (1, 12, 15, 2100), (5, 4, 11, 1000),
+TILE_CASES = [(1, 4, 9, 1000), (1, 12, 11, 2100), (2, 8, 14, 1000), (1, 12, 15, 2100), (2, 8, 11, 1000),
               (2, 8, 13, 2100), (3, 10, 15, 2100), (7, 6, 10, 2100), (5, 4, 13, 1000)]
 
 
@@ -362,7 +362,7 @@ def test_tile_kernel_every_sub_tile_count(B, gamma, K, V):
 # vocabularies of whole 64-column panels: the tile kernel's instance without
 # per-column tests; 1152 = 18 panels, so the last group of four holds two
 # panels past the vocabulary, 1024 = 16 panels in four whole groups
-WHOLE_PANEL_CASES = [(1, 12, 15, 1152), (3, 10, 15, 1152), (2, 8, 14, 1024), (5, 4, 11, 1152), (5, 4, 13, 1152),
+WHOLE_PANEL_CASES = [(1, 12, 15, 1152), (3, 10, 15, 1152), (2, 8, 14, 1024), (2, 8, 11, 1152), (5, 4, 13, 1152),
                      (7, 6, 10, 1024)]
 
 
