@@ -671,12 +671,15 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // into a D-deep register ring: the weight never passes through LDS.  Every
 // wave issues the same loads at every stage (a wave short of a masked-row
 // fragment copies one into a spare LDS area; stages past the end re-read the
-// last one into slots never read), so every wait is an exact count.  Per
-// stage a wave issues the loads of the stage D - 1 ahead, multiplies the
-// current one (4 x MSUB v_mfma_f32_16x16x32_bf16; 16x16x4 for fp32), waits
-// until its loads of the next stage have landed and meets the other waves at
-// a bare s_barrier (the workgroup fence of an ordinary barrier would also
-// wait for the loads of the later stages still in flight).
+// last one into slots never read), so every wait is an exact count.  Up to
+// eight sub-tiles, per stage a wave issues the loads of the stage D - 1
+// ahead, multiplies the current one (4 x MSUB v_mfma_f32_16x16x32_bf16;
+// 16x16x4 for fp32), waits until its loads of the next stage have landed and
+// meets the other waves at a bare s_barrier (the workgroup fence of an
+// ordinary barrier would also wait for the loads of the later stages still
+// in flight).  At nine and ten sub-tiles the registers hold only two stages
+// of W beyond the accumulators, so the stages go in pairs: one pair in
+// flight while the other is multiplied, and one barrier per pair.
 //
 // Two workgroups share a CU, each meeting only its own barrier, so one feeds
 // the matrix cores while the other waits.  Blocks are mapped so that the
@@ -692,11 +695,15 @@ __global__ __launch_bounds__(kPanelWaves * 64, DEEP ? 1 : 2) void k_gemm_panel(c
 // =====================================================================
 constexpr int kTileWaves = 4;  // 64-column panels per workgroup, one wave each
 
-// Stages in both rings (D - 1 in flight): the register ring of W holds D
-// stages of 16 VGPRs beside the 16 * MSUB accumulators.
+// The LDS ring holds D = 4 stages.  Up to eight sub-tiles the register ring
+// of W holds four single stages (16 VGPRs each, three in flight) and the
+// waves meet once per stage; at nine and ten sub-tiles, where the 16 * MSUB
+// accumulators leave room for 64 ring registers only, it holds two pairs of
+// stages (one pair in flight) and the waves meet once per pair.
 template <int MSUB>
 struct TileShape {
-    static constexpr int D = MSUB >= 9 ? 3 : 4;
+    static constexpr int D = 4;
+    static constexpr bool PAIRS = MSUB >= 9;
     static constexpr int NA = (MSUB + kTileWaves - 1) / kTileWaves;  // masked-row loads per wave per stage
     static constexpr int STAGE = MSUB * 1024;
     static constexpr int SPARE = D * STAGE;  // where a wave short of a fragment loads one
@@ -751,16 +758,16 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
     const uint8_t* wsrc = Wp + (size_t)min(my_panel, P.n_panels - 1) * nkb * (G * 1024) + lane * 16;
     const uint8_t* asrc = Hp + (size_t)tile * nkb * TS::STAGE + lane * 16;
 
-    v4u wr[D][G];
-    auto load_w = [&](int slot, int st) {
+    // the four W fragments of stage st (clamped to the last stage) into w
+    auto load_w = [&](v4u (&w)[G], int st) {
         const uint8_t* s = wsrc + (size_t)min(st, nkb - 1) * (G * 1024);
 #pragma unroll
-        for (int g = 0; g < G; ++g) wr[slot][g] = *(const v4u*)(s + g * 1024);
+        for (int g = 0; g < G; ++g) w[g] = *(const v4u*)(s + g * 1024);
     };
-    // fragments wave, wave + 4, ... of stage st into ring slot st % D
-    auto load_a = [&](int st) {
+    // fragments wave, wave + 4, ... of stage st (clamped) into LDS ring stage `slot`
+    auto load_a = [&](int st, int slot) {
         const uint8_t* s = asrc + (size_t)min(st, nkb - 1) * TS::STAGE;
-        uint8_t* base = ring + (st % D) * TS::STAGE;
+        uint8_t* base = ring + slot * TS::STAGE;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int f = wave + kTileWaves * j;
@@ -801,22 +808,54 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void k_gemm_tile(const Plan P, 
         }
     };
 
-    // One uniform loop: trips of D stages, so the register ring's slots are
-    // fixed.  Stage st issues the loads of stage st + D - 1 and multiplies
-    // stage st; the loop starts D - 1 stages early (loads only) and runs past
-    // the last stage (clamped loads, no products).  Without a separate
-    // prologue the compiler sees the same loads on every path into the loop,
-    // so its own waits for the register ring stay exact counts.
-    const int n_trips = (nkb + 2 * D - 2) / D;
-    for (int trip = 0; trip < n_trips; ++trip) {
+    if constexpr (TS::PAIRS) {
+        // Pair q of stages (2q, 2q + 1) sits in register slot q % 2 and LDS
+        // stages 2 (q % 2), + 1.  Each block waits for every load (only the
+        // current pair's are in flight), meets the other waves (so the other
+        // slot's LDS stages are free), issues the next pair and multiplies
+        // the current one.  The wait opens the block, so the compiler sees it
+        // on every path into the products and adds none of its own.
+        v4u wr[2][2][G];
+        auto load_pair = [&](int slot, int q) {
 #pragma unroll
-        for (int k = 0; k < D; ++k) {
-            const int st = trip * D + k - (D - 1);
-            load_w((k + D - 1) % D, st + D - 1);
-            load_a(st + D - 1);
-            if (st >= 0 && st < nkb) mma(wr[k], ring + (st % D) * TS::STAGE + lane * 16);
-            wait_vmcnt<(D - 2) * (G + NA)>();
-            ring_barrier();
+            for (int h2 = 0; h2 < 2; ++h2) {
+                load_w(wr[slot][h2], 2 * q + h2);
+                load_a(2 * q + h2, 2 * slot + h2);
+            }
+        };
+        const int npairs = (nkb + 1) / 2;
+        load_pair(0, 0);
+        for (int pr = 0; pr < npairs; pr += 2) {
+#pragma unroll
+            for (int slot = 0; slot < 2; ++slot) {
+                const int q = pr + slot;
+                wait_vmcnt<0>();
+                ring_barrier();
+                load_pair(slot ^ 1, q + 1);
+                if (2 * q < nkb) mma(wr[slot][0], ring + (2 * slot) * TS::STAGE + lane * 16);
+                if (2 * q + 1 < nkb) mma(wr[slot][1], ring + (2 * slot + 1) * TS::STAGE + lane * 16);
+            }
+        }
+    } else {
+        // One uniform loop: trips of D stages, so the register ring's slots
+        // are fixed.  Stage st issues the loads of stage st + D - 1 and
+        // multiplies stage st; the loop starts D - 1 stages early (loads
+        // only) and runs past the last stage (clamped loads, no products).
+        // Without a separate prologue the compiler sees the same loads on
+        // every path into the loop, so its own waits for the register ring
+        // stay exact counts.
+        v4u wr[D][G];
+        const int n_trips = (nkb + 2 * D - 2) / D;
+        for (int trip = 0; trip < n_trips; ++trip) {
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                const int st = trip * D + k - (D - 1);
+                load_w(wr[(k + D - 1) % D], st + D - 1);
+                load_a(st + D - 1, (st + D - 1) % D);
+                if (st >= 0 && st < nkb) mma(wr[k], ring + (st % D) * TS::STAGE + lane * 16);
+                wait_vmcnt<(D - 2) * (G + NA)>();
+                ring_barrier();
+            }
         }
     }
     wait_vmcnt<0>();
