@@ -403,6 +403,18 @@ def test_tile_kernel_half_lossless_half_naive():
     _check(w.W, w.h, w.draft, w.q_hat, np.full(8, wl.JS, np.uint8), 8, 0.2, [5], layout=P.PANELS)
 
 
+@pytest.mark.parametrize("d", [64, 128, 192])
+def test_tile_kernel_short_reductions(d):
+    """Ten and nine sub-tiles, whose main loop runs the reduction in pairs of
+    64-byte stages, over reductions of one, two and three pairs (bf16 rows of
+    64, 128 and 192 elements): the first pair is also the last, and the loads
+    past the end are clamped."""
+    for B, gamma, K in ((2, 8, 13), (2, 8, 11)):
+        assert _tile_choice(B * (gamma + 1), K)[0] in (9, 10)
+        w = wl.generate(1, B=B, gamma=gamma, d=d, V=1152, K=K, planted=0.8)
+        _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, [3], layout=P.PANELS)
+
+
 def test_calls_on_one_handle_carry_no_state(layout):
     """Consecutive calls on one handle, each with a different set of lossless
     sequences (whose residual races meet in per-sequence workspace slots),
