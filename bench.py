@@ -108,6 +108,14 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def ragged_gammas(cfg, seed: int):
+    """The per-sequence draft counts of `--ragged SEED`: uniform on
+    0..gamma, one per sequence, from numpy's default generator."""
+    import numpy as np
+
+    return np.random.default_rng(seed).integers(0, cfg.gamma + 1, cfg.B).astype(np.int32)
+
+
 def cpu_info():
     """(CPU model string, nproc, CPUs this process may run on)."""
     model = None
@@ -290,7 +298,7 @@ def main():
 
     seq_gamma = None
     if args.ragged:
-        seq_gamma = np.random.default_rng(args.ragged).integers(0, cfg.gamma + 1, cfg.B).astype(np.int32)
+        seq_gamma = ragged_gammas(cfg, args.ragged)
 
     def step_on(st):
         ver.run(W_run, h, draft, q_hat, w.modes, cfg.K, cfg.p_drop, seed, stream=st.cuda_stream, outputs=outs,

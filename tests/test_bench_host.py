@@ -20,9 +20,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMMS = ("k_gemm_panel", "k_gemm_tile", "k_gemm_skinny")
 
 
-def _kernel(cfg, panels=True):
-    n_lossless = int((wl.modes_for(cfg) == wl.LOSSLESS).sum())
-    return bench.gemm_kernel(cfg, panels, n_lossless)
+def _kernel(cfg, panels=True, ragged_seed=0):
+    modes = wl.modes_for(cfg)
+    n_lossless = int((modes == wl.LOSSLESS).sum())
+    if not ragged_seed:
+        return bench.gemm_kernel(cfg, panels, n_lossless)
+    per_seq = bench.ragged_gammas(cfg, ragged_seed) + 1
+    lossless = modes == wl.LOSSLESS
+    return bench.gemm_kernel(cfg, panels, n_lossless, int(per_seq[~lossless].sum()), int(per_seq[lossless].sum()))
 
 
 def test_kernel_rule_per_workload():
@@ -53,11 +58,11 @@ def test_kernel_rule_matches_the_recorded_traces():
     by_name = {cfg.name: cfg for cfg in wl.CONFIGS}
     seen = 0
     for path in traces:
-        m = re.match(r"(k_gemm_[a-z]+)_(.+)_kernel_trace\.md$", os.path.basename(path))
+        m = re.match(r"(k_gemm_[a-z]+)_(.+?)(_ragged(\d+))?_kernel_trace\.md$", os.path.basename(path))
         assert m, path
         cfg = by_name[m.group(2)]
         launched = {k for k in GEMMS if f"dmv::{k}" in open(path).read()}
-        assert launched == {_kernel(cfg)} == {m.group(1)}, path
+        assert launched == {_kernel(cfg, ragged_seed=int(m.group(4) or 0))} == {m.group(1)}, path
         seen += 1
     assert seen >= 2
 

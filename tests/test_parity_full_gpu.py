@@ -88,8 +88,9 @@ def test_config3_batched_70b_ragged():
     """The ragged batch bench.py --ragged 7 times: each sequence's draft
     count drawn from 0..gamma with generator seed 7 (153 of 256 positions
     live, five 160-row tiles), on a window of 8 sequences per seed."""
-    cfg = wl.CONFIGS[3]
-    seq_gamma = np.random.default_rng(7).integers(0, cfg.gamma + 1, cfg.B).astype(np.int32)
+    import bench
+
+    seq_gamma = bench.ragged_gammas(wl.CONFIGS[3], 7)
     _full(3, per_seed=8, seeds=range(1, 5), ragged=dict(seq_gamma=seq_gamma))
 
 
