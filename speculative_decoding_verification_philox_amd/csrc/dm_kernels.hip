@@ -1394,9 +1394,11 @@ __device__ __forceinline__ int tree_walk(bool live, bool pass, int up, int lane,
     return key >> 6;
 }
 
-// JS partial sums of one (position, chunk): kJsPerThread consecutive entries
-// per thread, every load issued before any arithmetic (float4 loads when
-// rows are 16-byte aligned).  KMAX bounds K so the registers stay small.
+// JS partial sums of one (position, chunk): kJsPerThread entries per
+// thread, every load issued before any arithmetic.  Rows 16-byte aligned:
+// thread x takes float4s at 4x and 4x + 1024 of the chunk, so each wave's
+// load covers 1 KiB contiguous; otherwise entries x, x + 256, ....  KMAX
+// bounds K so the registers stay small.
 template <int KMAX>
 __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __restrict__ q_hat,
                                          const float* __restrict__ logits, const RowStat* __restrict__ rowstat,
@@ -1414,7 +1416,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     const int pidx = b * T1 + t;
     const float* lrow = logits + (size_t)pidx * K * V;
     const float* qrow = q_hat + (size_t)(b * G + t) * V;
-    const int v0 = c * P.js_chunk + threadIdx.x * E;
+    const int v0 = c * P.js_chunk;
 
     // Loads past the end of the vocabulary read a valid entry instead and are
     // zeroed, so no lane branches; q = -1 marks them.
@@ -1422,8 +1424,9 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     if (P.vec4) {
 #pragma unroll
         for (int u = 0; u < E; u += 4) {
-            const bool ok = v0 + u < V;  // V % 4 == 0: a float4 is wholly in or out
-            const int vv = ok ? v0 + u : V - 4;
+            const int vu = v0 + u * kVocabThreads + 4 * threadIdx.x;  // a wave reads 1 KiB contiguous
+            const bool ok = vu < V;  // V % 4 == 0: a float4 is wholly in or out
+            const int vv = ok ? vu : V - 4;
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 v4f x = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1438,8 +1441,9 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     } else {
 #pragma unroll
         for (int u = 0; u < E; ++u) {
-            const bool ok = v0 + u < V;
-            const int vv = ok ? v0 + u : V - 1;
+            const int vu = v0 + u * kVocabThreads + threadIdx.x;
+            const bool ok = vu < V;
+            const int vv = ok ? vu : V - 1;
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 float x = 0.0f;
