@@ -403,6 +403,19 @@ def test_tile_kernel_half_lossless_half_naive():
     _check(w.W, w.h, w.draft, w.q_hat, np.full(8, wl.JS, np.uint8), 8, 0.2, [5], layout=P.PANELS)
 
 
+def test_tile_kernel_odd_vocabulary():
+    """|V| = 3001: the last panel is cut after 57 columns and rows are not
+    16-byte aligned, so the tile kernel stores 4 bytes per lane and masks the
+    cut panel's columns; at ten sub-tiles (pairs of stages) and at eight."""
+    for B, gamma, K in ((2, 8, 13), (2, 6, 15)):
+        ms, tiles = _tile_choice(B * (gamma + 1), K)
+        assert tiles >= 2 and ms in (8, 10), (ms, tiles)
+        w = wl.generate(1, B=B, gamma=gamma, d=320, V=3001, K=K, planted=0.8)
+        _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, [4], layout=P.PANELS)
+        modes = np.arange(B, dtype=np.uint8) % 3
+        _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.3, [6], layout=P.PANELS)
+
+
 @pytest.mark.parametrize("d", [64, 128, 192])
 def test_tile_kernel_short_reductions(d):
     """Ten and nine sub-tiles, whose main loop runs the reduction in pairs of
