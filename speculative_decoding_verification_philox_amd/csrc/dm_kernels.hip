@@ -1395,7 +1395,8 @@ __device__ __forceinline__ int tree_walk(bool live, bool pass, int up, int lane,
 }
 
 // JS partial sums of one (position, chunk): kJsPerThread entries per
-// thread, every load issued before any arithmetic.  Rows 16-byte aligned:
+// thread, every load issued before any arithmetic, all non-temporal (each
+// logit and q_hat entry is read once per call).  Rows 16-byte aligned:
 // thread x takes float4s at 4x and 4x + 1024 of the chunk, so each wave's
 // load covers 1 KiB contiguous; otherwise entries x, x + 256, ....  KMAX
 // bounds K so the registers stay small.
@@ -1430,11 +1431,11 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 v4f x = v4f{0.f, 0.f, 0.f, 0.f};
-                if (i < Kb) x = *(const v4f*)(lrow + (size_t)i * V + vv);  // Kb is uniform
+                if (i < Kb) x = __builtin_nontemporal_load((const v4f*)(lrow + (size_t)i * V + vv));  // Kb is uniform
 #pragma unroll
                 for (int e = 0; e < 4; ++e) l[u + e][i] = ok ? x[e] : 0.0f;
             }
-            const v4f y = *(const v4f*)(qrow + vv);
+            const v4f y = __builtin_nontemporal_load((const v4f*)(qrow + vv));
 #pragma unroll
             for (int e = 0; e < 4; ++e) q[u + e] = ok ? y[e] : -1.0f;
         }
@@ -1447,10 +1448,10 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
                 float x = 0.0f;
-                if (i < Kb) x = lrow[(size_t)i * V + vv];
+                if (i < Kb) x = __builtin_nontemporal_load(lrow + (size_t)i * V + vv);
                 l[u][i] = ok ? x : 0.0f;
             }
-            const float y = qrow[vv];
+            const float y = __builtin_nontemporal_load(qrow + vv);
             q[u] = ok ? y : -1.0f;
         }
     }
@@ -1546,8 +1547,8 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const bool ok = vq + k < v1;
-            lv[k] = ok ? lrow[vq + k] : 0.0f;
-            qv[k] = (ok && qrow) ? qrow[vq + k] : 0.0f;
+            lv[k] = ok ? __builtin_nontemporal_load(lrow + vq + k) : 0.0f;
+            qv[k] = (ok && qrow) ? __builtin_nontemporal_load(qrow + vq + k) : 0.0f;
         }
         const u32x4 rr = philox10(u32x4{(uint32_t)(vq >> 2), (uint32_t)pidx, 0u, kStreamRace}, P.key0, P.key1);
         const uint32_t words[4] = {rr.x, rr.y, rr.z, rr.w};
