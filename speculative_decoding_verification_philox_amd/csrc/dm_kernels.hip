@@ -1400,7 +1400,7 @@ __device__ __forceinline__ int tree_walk(bool live, bool pass, int up, int lane,
 // thread x takes float4s at 4x and 4x + 1024 of the chunk, so each wave's
 // load covers 1 KiB contiguous; otherwise entries x, x + 256, ....  KMAX
 // bounds K so the registers stay small.
-template <int KMAX>
+template <int KMAX, bool VEC4>
 __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __restrict__ q_hat,
                                          const float* __restrict__ logits, const RowStat* __restrict__ rowstat,
                                          const RowStat* __restrict__ centstat, float* __restrict__ jspart,
@@ -1419,10 +1419,12 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     const float* qrow = q_hat + (size_t)(b * G + t) * V;
     const int v0 = c * P.js_chunk;
 
-    // Loads past the end of the vocabulary read a valid entry instead and are
-    // zeroed, so no lane branches; q = -1 marks them.
+    // Loads past the end of the vocabulary read a valid entry instead, so no
+    // lane branches; such an entry takes live = 0, which zeroes every
+    // probability it contributes (the values it read stay finite).
     float l[E][KMAX], q[E];
-    if (P.vec4) {
+    bool live[E];
+    if constexpr (VEC4) {
 #pragma unroll
         for (int u = 0; u < E; u += 4) {
             const int vu = v0 + u * kVocabThreads + 4 * threadIdx.x;  // a wave reads 1 KiB contiguous
@@ -1433,11 +1435,14 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
                 v4f x = v4f{0.f, 0.f, 0.f, 0.f};
                 if (i < Kb) x = __builtin_nontemporal_load((const v4f*)(lrow + (size_t)i * V + vv));  // Kb is uniform
 #pragma unroll
-                for (int e = 0; e < 4; ++e) l[u + e][i] = ok ? x[e] : 0.0f;
+                for (int e = 0; e < 4; ++e) l[u + e][i] = x[e];
             }
             const v4f y = __builtin_nontemporal_load((const v4f*)(qrow + vv));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) q[u + e] = ok ? y[e] : -1.0f;
+            for (int e = 0; e < 4; ++e) {
+                q[u + e] = y[e];
+                live[u + e] = ok;
+            }
         }
     } else {
 #pragma unroll
@@ -1449,10 +1454,10 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
             for (int i = 0; i < KMAX; ++i) {
                 float x = 0.0f;
                 if (i < Kb) x = __builtin_nontemporal_load(lrow + (size_t)i * V + vv);
-                l[u][i] = ok ? x : 0.0f;
+                l[u][i] = x;
             }
-            const float y = __builtin_nontemporal_load(qrow + vv);
-            q[u] = ok ? y : -1.0f;
+            q[u] = __builtin_nontemporal_load(qrow + vv);
+            live[u] = ok;
         }
     }
     float logz[KMAX];
@@ -1465,7 +1470,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     for (int i = 0; i <= KMAX; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-        const float live = q[u] < 0.0f ? 0.0f : 1.0f;  // 0 past the end of the vocabulary
+        const float lv = live[u] ? 1.0f : 0.0f;  // 0 past the end of the vocabulary
         // the centroid logit, same operations in the same order as the
         // LM-head epilogue's
         float lsum = l[u][0];
@@ -1473,14 +1478,14 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
         for (int i = 1; i < KMAX; ++i)
             if (i < Kb) lsum += l[u][i];
         const float bb = lsum * inv_k - logz_c;
-        const float pb = hw_exp(bb) * live;
+        const float pb = hw_exp(bb) * lv;
 #pragma unroll
         for (int i = 0; i < KMAX; ++i)
             if (i < Kb) {
                 const float a = l[u][i] - logz[i];
-                acc[i] += js_entry(a, hw_exp(a) * live, bb, pb);
+                acc[i] += js_entry(a, hw_exp(a) * lv, bb, pb);
             }
-        const float qq = fmaxf(q[u], 0.0f);
+        const float qq = live[u] ? fmaxf(q[u], 0.0f) : 0.0f;
         acc[KMAX] += js_entry(hw_log(fmaxf(qq, kMixFloor)), qq, bb, pb);
     }
 #pragma unroll
@@ -1502,7 +1507,11 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 // KMAX bounds the heads the JS blocks hold in registers; the launch picks
 // the smallest of 5, 8 and kMaxK that covers K, so a kernel's register
 // budget (and with it how many waves a CU keeps in flight) follows K.
-template <int KMAX>
+// VEC4: the rows are read as float4 (16-byte aligned, V % 4 == 0).  The
+// scalar path is an instance of its own because a kernel's register count
+// is the largest over its code: in one instance with the float4 path it
+// held K <= 5 at 66 VGPRs (7 waves per SIMD) instead of 62 (8 waves).
+template <int KMAX, bool VEC4>
 __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const Plan P, const int32_t* __restrict__ draft, const float* __restrict__ q_hat,
     const float* __restrict__ logits, const RowStat* __restrict__ rowstat, const RowStat* __restrict__ centstat,
@@ -1515,7 +1524,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     (void)wave;
 
     if (blk < P.blk_js) {
-        js_block<KMAX>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
+        js_block<KMAX, VEC4>(P, blk, q_hat, logits, rowstat, centstat, jspart, s_red);
         return;
     }
     blk -= P.blk_js;
@@ -2202,15 +2211,13 @@ hipError_t launch_vocab(const Plan& P, const int32_t* draft, const float* q_hat,
                         float* dbg_js_draft, hipStream_t st) {
     if (P.blk_js + P.blk_race > 0) {
         const dim3 grid(P.blk_js + P.blk_race), block(kVocabThreads);
+        auto kernel = P.vec4 ? k_vocab<kMaxK, true> : k_vocab<kMaxK, false>;
         if (P.K <= 5)
-            hipLaunchKernelGGL(k_vocab<5>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
-                               race_best, filt);
+            kernel = P.vec4 ? k_vocab<5, true> : k_vocab<5, false>;
         else if (P.K <= 8)
-            hipLaunchKernelGGL(k_vocab<8>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart,
-                               race_best, filt);
-        else
-            hipLaunchKernelGGL(k_vocab<kMaxK>, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat,
-                               jspart, race_best, filt);
+            kernel = P.vec4 ? k_vocab<8, true> : k_vocab<8, false>;
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, P, draft, q_hat, logits, rowstat, centstat, jspart, race_best,
+                           filt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
