@@ -13,6 +13,10 @@ constexpr int kMaxK = 16;
 constexpr int kMaxGamma = 63;  // drafts (tree nodes) per sequence: positions fit one wave
 constexpr int kMaskWords = kMaxBatch / 32;
 constexpr int kMaxDropValues = 8;  // distinct per-sequence dropout probabilities in one call
+// 64-bit words per sequence in the residual-race slots: its two slots alone
+// in a 128-byte line, so the atomics of different sequences never share one
+constexpr int kRaceSlotStride = 16;
+constexpr int kRaceChunkMax = 4096;  // vocabulary entries of one residual-race block
 
 enum Mode : int { kLossless = 0, kNaive = 1, kJs = 2, kTreeNaive = 3 };
 

@@ -1230,7 +1230,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (t == 0)
-        for (int i = threadIdx.x; i < 2 * P.B; i += kCombineThreads) race_best[i] = 0ull;
+        for (int i = threadIdx.x; i < P.B; i += kCombineThreads) {
+            race_best[kRaceSlotStride * i] = 0ull;
+            race_best[kRaceSlotStride * i + 1] = 0ull;
+        }
     int b, pos_t, head = 0;
     const bool is_row = t < P.R_phys;
     bool lossless = false;
@@ -1298,6 +1301,9 @@ constexpr int kVocabThreads = 256;
 constexpr int kVocabWaves = kVocabThreads / 64;
 constexpr int kJsPerThread = 8;  // the JS chunk is kVocabThreads * kJsPerThread entries
 constexpr float kLn2 = 0.69314718055994531f;
+// steps of 4 entries per thread that cover one race block's chunk
+constexpr int kRaceSteps = kRaceChunkMax / (4 * kVocabThreads);
+static_assert(kRaceSteps * 4 * kVocabThreads == kRaceChunkMax, "race chunk: whole steps");
 
 // e^x and ln x on the hardware base-2 units (v_exp_f32, v_log_f32), for
 // arguments whose results stay in the normal fp32 range.
@@ -1518,6 +1524,7 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     float* __restrict__ jspart, unsigned long long* __restrict__ race_best, const FiltStat* __restrict__ filt) {
     __shared__ float s_red[kVocabWaves][kMaxK + 1];
     __shared__ int s_A;
+    __shared__ unsigned long long s_best[2][kVocabWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = P.K, G = P.G, T1 = P.T1, V = P.V;
     int blk = blockIdx.x;
@@ -1550,23 +1557,43 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
     const float* qrow = A < Gb ? q_hat + (size_t)(b * G + A) * V : nullptr;
     unsigned long long best_r = 0ull, best_p = 0ull;
     const int v0 = c * P.race_chunk;
-    const int v1 = min(v0 + P.race_chunk, V);
-    for (int vq = v0 + 4 * threadIdx.x; vq < v1; vq += 4 * kVocabThreads) {
-        float lv[4], qv[4];
+    const int v1 = min(v0 + P.race_chunk, V);  // race_chunk <= kRaceChunkMax, a multiple of 1024
+    // every load of the chunk first (non-temporal: read once per call); an
+    // entry past the chunk reads a valid one and is skipped below
+    float lv[kRaceSteps][4], qv[kRaceSteps][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool ok = vq + k < v1;
-            lv[k] = ok ? __builtin_nontemporal_load(lrow + vq + k) : 0.0f;
-            qv[k] = (ok && qrow) ? __builtin_nontemporal_load(qrow + vq + k) : 0.0f;
+    for (int it = 0; it < kRaceSteps; ++it) {
+        const int vq = v0 + 4 * threadIdx.x + it * 4 * kVocabThreads;
+        if constexpr (VEC4) {  // V % 4 == 0, so v1 % 4 == 0: a float4 is wholly in or out
+            const int vv = vq < v1 ? vq : V - 4;
+            const v4f x = __builtin_nontemporal_load((const v4f*)(lrow + vv));
+            const v4f y = qrow ? __builtin_nontemporal_load((const v4f*)(qrow + vv)) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                lv[it][k] = x[k];
+                qv[it][k] = y[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int vv = vq + k < v1 ? vq + k : V - 1;
+                lv[it][k] = __builtin_nontemporal_load(lrow + vv);
+                qv[it][k] = qrow ? __builtin_nontemporal_load(qrow + vv) : 0.0f;
+            }
         }
+    }
+#pragma unroll
+    for (int it = 0; it < kRaceSteps; ++it) {
+        const int vq = v0 + 4 * threadIdx.x + it * 4 * kVocabThreads;
+        if (vq >= v1) break;  // later steps are past the chunk too
         const u32x4 rr = philox10(u32x4{(uint32_t)(vq >> 2), (uint32_t)pidx, 0u, kStreamRace}, P.key0, P.key1);
         const uint32_t words[4] = {rr.x, rr.y, rr.z, rr.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int v = vq + k;
             if (v >= v1) continue;
-            const float p = lv[k] >= thresh ? __expf(lv[k] - logz) : 0.0f;
-            const float w = qrow ? fmaxf(p - qv[k], 0.0f) : p;
+            const float p = lv[it][k] >= thresh ? __expf(lv[it][k] - logz) : 0.0f;
+            const float w = qrow ? fmaxf(p - qv[it][k], 0.0f) : p;
             // U in (0, 1): top 23 bits plus one half, times 2^-23
             const float U = ((float)(words[k] >> 9) + 0.5f) * 1.1920928955078125e-07f;
             const float E = -__logf(U);
@@ -1579,9 +1606,20 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
         best_r = u64_max(best_r, __shfl_xor(best_r, off, 64));
         best_p = u64_max(best_p, __shfl_xor(best_p, off, 64));
     }
+    // the waves' winners meet in LDS, so a block takes one atomic per slot
     if (lane == 0) {
-        if (best_r) atomicMax(&race_best[2 * b], best_r);
-        if (best_p) atomicMax(&race_best[2 * b + 1], best_p);
+        s_best[0][wave] = best_r;
+        s_best[1][wave] = best_p;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kVocabWaves; ++w) {
+            best_r = u64_max(best_r, s_best[0][w]);
+            best_p = u64_max(best_p, s_best[1][w]);
+        }
+        if (best_r) atomicMax(&race_best[kRaceSlotStride * b], best_r);
+        if (best_p) atomicMax(&race_best[kRaceSlotStride * b + 1], best_p);
     }
 }
 
@@ -1646,8 +1684,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(const Plan P, const i
                     if (i < Kb) head_idx[i] = rowstat[(b * T1 + at) * K + i].idx;
             }
         } else if (lane == 0) {
-            best_r = race_best[2 * b];
-            best_p = race_best[2 * b + 1];
+            best_r = race_best[kRaceSlotStride * b];
+            best_p = race_best[kRaceSlotStride * b + 1];
         }
     }
 

@@ -210,6 +210,7 @@ void make_plan(const dm_verify_desc& D, int B, int K, int n_lossless, int n_js, 
         const int chmax = cdiv(P.V, 1024);
         ch = ch < 1 ? 1 : (ch > chmax ? chmax : ch);
         P.race_chunk = cdiv(cdiv(P.V, ch), 1024) * 1024;
+        if (P.race_chunk > kRaceChunkMax) P.race_chunk = kRaceChunkMax;  // a block holds at most this many
         P.race_chunks = cdiv(P.V, P.race_chunk);
     }
     P.blk_js = P.n_js_pos * P.js_chunks;
@@ -248,7 +249,7 @@ Sizes workspace_sizes(const dm_verify_desc& D) {
     s.centstat = (size_t)D.max_batch * T1 * sizeof(RowStat);
     s.meta = max_hm_rows * sizeof(RowMeta);
     s.jspart = (max_js > 0 ? max_js : 1) * sizeof(float);
-    s.race = (size_t)D.max_batch * 2 * sizeof(unsigned long long);
+    s.race = (size_t)D.max_batch * kRaceSlotStride * sizeof(unsigned long long);
     s.filt = (size_t)D.max_batch * T1 * sizeof(FiltStat);
     return s;
 }
@@ -272,7 +273,7 @@ Sizes plan_sizes(const dm_verify_desc& D, const Plan& P) {
     s.centstat = rows * sizeof(RowStat);
     s.meta = (size_t)P.R_phys * sizeof(RowMeta);
     s.jspart = ((size_t)P.n_js_pos * P.js_chunks * (P.K + 1) + 1) * sizeof(float);
-    s.race = (size_t)P.B * 2 * sizeof(unsigned long long);
+    s.race = (size_t)P.B * kRaceSlotStride * sizeof(unsigned long long);
     s.filt = rows * sizeof(FiltStat);
     return s;
 }
