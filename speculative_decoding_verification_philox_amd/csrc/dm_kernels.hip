@@ -1314,13 +1314,14 @@ __device__ __forceinline__ float hw_log(float x) { return __builtin_amdgcn_logf(
 // probabilities sum to less contributes below 1e-36 and is left at that.
 constexpr float kMixFloor = 1e-37f;
 
-// One vocabulary entry's share of JS(P || Q): with a = ln P, b = ln Q and
-// ln M = ln(P + Q) - ln 2, it is (P (a - ln M) + Q (b - ln M)) / 2.  A zero
-// probability contributes nothing as long as its log argument is finite.
-// Branch-free.
-__device__ __forceinline__ float js_entry(float a, float Pa, float b, float Pb) {
-    const float lm = hw_log(fmaxf(Pa + Pb, kMixFloor)) - kLn2;
-    return 0.5f * (Pa * (a - lm) + Pb * (b - lm));
+// Adds twice one vocabulary entry's share of JS(P || Q) to acc: with
+// a = ln P, b = ln Q and ln M = ln(P + Q) - ln 2 = ln 2 (log2(P + Q) - 1),
+// the share is (P (a - ln M) + Q (b - ln M)) / 2; the factor 1/2 is applied
+// once to the chunk sum.  A zero probability contributes nothing as long as
+// its log argument is finite.  Branch-free.
+__device__ __forceinline__ float js_acc2(float acc, float a, float Pa, float b, float Pb) {
+    const float lm = fmaf(__builtin_amdgcn_logf(fmaxf(Pa + Pb, kMixFloor)), kLn2, -kLn2);
+    return fmaf(Pb, b - lm, fmaf(Pa, a - lm, acc));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -1489,10 +1490,10 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
         for (int i = 0; i < KMAX; ++i)
             if (i < Kb) {
                 const float a = l[u][i] - logz[i];
-                acc[i] += js_entry(a, hw_exp(a) * lv, bb, pb);
+                acc[i] = js_acc2(acc[i], a, hw_exp(a) * lv, bb, pb);
             }
         const float qq = live[u] ? fmaxf(q[u], 0.0f) : 0.0f;
-        acc[KMAX] += js_entry(hw_log(fmaxf(qq, kMixFloor)), qq, bb, pb);
+        acc[KMAX] = js_acc2(acc[KMAX], hw_log(fmaxf(qq, kMixFloor)), qq, bb, pb);
     }
 #pragma unroll
     for (int i = 0; i <= KMAX; ++i)
@@ -1506,7 +1507,7 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
         float x = 0.0f;
 #pragma unroll
         for (int w = 0; w < kVocabWaves; ++w) x += s_red[w][i];
-        jspart[((size_t)jp * (K + 1) + threadIdx.x) * P.js_chunks + c] = x;
+        jspart[((size_t)jp * (K + 1) + threadIdx.x) * P.js_chunks + c] = 0.5f * x;
     }
 }
 
@@ -1594,11 +1595,13 @@ __global__ __launch_bounds__(kVocabThreads) void k_vocab(
             if (v >= v1) continue;
             const float p = lv[it][k] >= thresh ? __expf(lv[it][k] - logz) : 0.0f;
             const float w = qrow ? fmaxf(p - qv[it][k], 0.0f) : p;
-            // U in (0, 1): top 23 bits plus one half, times 2^-23
+            // U in (0, 1): top 23 bits plus one half, times 2^-23, a normal
+            // number, so the hardware log2 needs no range reduction; the
+            // keys take one reciprocal of E = -ln U
             const float U = ((float)(words[k] >> 9) + 0.5f) * 1.1920928955078125e-07f;
-            const float E = -__logf(U);
-            if (w > 0.0f) best_r = u64_max(best_r, race_pack(w / E, v));
-            if (p > 0.0f) best_p = u64_max(best_p, race_pack(p / E, v));
+            const float inv_e = __builtin_amdgcn_rcpf(-kLn2 * __builtin_amdgcn_logf(U));
+            if (w > 0.0f) best_r = u64_max(best_r, race_pack(w * inv_e, v));
+            if (p > 0.0f) best_p = u64_max(best_p, race_pack(p * inv_e, v));
         }
     }
 #pragma unroll
