@@ -324,6 +324,7 @@ struct RowStat {
     float m;
     float logz;
     int idx;
+    float logz1;  // logz - ln 2: the vocabulary pass takes its JS terms from logs shifted by ln 2
 };
 
 // The processed target of one lossless position: v is kept iff its logit is

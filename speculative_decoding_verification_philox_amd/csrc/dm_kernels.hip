@@ -1217,6 +1217,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(const Plan P, const 
 // call starts from empty slots whatever an earlier call left there.
 // =====================================================================
 constexpr int kCombineThreads = 256;
+constexpr float kLn2Combine = 0.69314718055994531f;
 
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const Stat* __restrict__ part,
                                                              RowStat* __restrict__ rowstat,
@@ -1267,7 +1268,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const Plan P, const
     st = s_w[0];
 #pragma unroll
     for (int w = 1; w < kCombineThreads / 64; ++w) st = stat_merge(st, s_w[w]);
-    const RowStat rs{st.m, st.m + __logf(st.s), st.idx};
+    const float logz = st.m + __logf(st.s);
+    const RowStat rs{st.m, logz, st.idx, logz - kLn2Combine};
     const int pidx = b * P.T1 + pos_t;
     if (is_row) {
         const int canon = pidx * P.K + head;
@@ -1314,15 +1316,20 @@ __device__ __forceinline__ float hw_log(float x) { return __builtin_amdgcn_logf(
 // probabilities sum to less contributes below 1e-36 and is left at that.
 constexpr float kMixFloor = 1e-37f;
 
-// Adds twice one vocabulary entry's share of JS(P || Q) to acc: with
-// a = ln P, b = ln Q and ln M = ln(P + Q) - ln 2 = ln 2 (log2(P + Q) - 1),
-// the share is (P (a - ln M) + Q (b - ln M)) / 2; the factor 1/2 is applied
-// once to the chunk sum.  A zero probability contributes nothing as long as
-// its log argument is finite.  Branch-free.
-__device__ __forceinline__ float js_acc2(float acc, float a, float Pa, float b, float Pb) {
-    const float lm = fmaf(__builtin_amdgcn_logf(fmaxf(Pa + Pb, kMixFloor)), kLn2, -kLn2);
-    return fmaf(Pb, b - lm, fmaf(Pa, a - lm, acc));
+// Adds twice one vocabulary entry's share of JS(P || Q) to acc.  With
+// a = ln P, b = ln Q and ln M = ln(P + Q) - ln 2 = ln 2 (L - 1), L =
+// log2(P + Q), the share is (P (a - ln M) + Q (b - ln M)) / 2.  The caller
+// passes the shifted logs a1 = a + ln 2 and b1 = b + ln 2, so that
+// a - ln M = a1 - ln 2 L (one fused multiply-add); the factor 1/2 is
+// applied once to the chunk sum.  A zero probability contributes nothing as
+// long as its log argument is finite.  Branch-free.
+__device__ __forceinline__ float js_acc2(float acc, float a1, float Pa, float b1, float Pb) {
+    const float L = __builtin_amdgcn_logf(fmaxf(Pa + Pb, kMixFloor));
+    return fmaf(Pb, fmaf(-kLn2, L, b1), fmaf(Pa, fmaf(-kLn2, L, a1), acc));
 }
+
+// P = e^a from the shifted log a1 = a + ln 2: 2^(a1 log2 e - 1).
+__device__ __forceinline__ float exp_shifted(float a1) { return __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, -1.0f)); }
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -1469,8 +1476,8 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
     }
     float logz[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) logz[i] = i < Kb ? rowstat[pidx * K + i].logz : 0.0f;
-    const float logz_c = centstat[pidx].logz;
+    for (int i = 0; i < KMAX; ++i) logz[i] = i < Kb ? rowstat[pidx * K + i].logz1 : 0.0f;  // log Z - ln 2
+    const float logz_c = centstat[pidx].logz1;
 
     float acc[KMAX + 1];
 #pragma unroll
@@ -1484,16 +1491,16 @@ __device__ __forceinline__ void js_block(const Plan& P, int blk, const float* __
 #pragma unroll
         for (int i = 1; i < KMAX; ++i)
             if (i < Kb) lsum += l[u][i];
-        const float bb = lsum * inv_k - logz_c;
-        const float pb = hw_exp(bb) * lv;
+        const float bb = lsum * inv_k - logz_c;  // ln p-bar + ln 2
+        const float pb = exp_shifted(bb) * lv;
 #pragma unroll
         for (int i = 0; i < KMAX; ++i)
             if (i < Kb) {
-                const float a = l[u][i] - logz[i];
-                acc[i] = js_acc2(acc[i], a, hw_exp(a) * lv, bb, pb);
+                const float a = l[u][i] - logz[i];  // ln p + ln 2
+                acc[i] = js_acc2(acc[i], a, exp_shifted(a) * lv, bb, pb);
             }
         const float qq = live[u] ? fmaxf(q[u], 0.0f) : 0.0f;
-        acc[KMAX] = js_acc2(acc[KMAX], hw_log(fmaxf(qq, kMixFloor)), qq, bb, pb);
+        acc[KMAX] = js_acc2(acc[KMAX], fmaf(__builtin_amdgcn_logf(fmaxf(qq, kMixFloor)), kLn2, kLn2), qq, bb, pb);
     }
 #pragma unroll
     for (int i = 0; i <= KMAX; ++i)
