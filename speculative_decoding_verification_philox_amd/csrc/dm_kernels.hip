@@ -111,33 +111,39 @@ __global__ __launch_bounds__(256) void k_prep(const Plan P, const void* __restri
 // k_prep_packed: the same masked rows, written in matrix-core operand order
 // (per tile: [fragment kb][sub-tile m][lane][16 B], lane 16 a + r holding
 // bytes 64 kb + 16 a .. + 16 of sub-tile row r) for the panel-order kernels.
-// One thread per 16-byte piece of the output, so consecutive threads write
-// consecutive bytes; the source row piece is gathered from h (L2-resident).
+// One thread per 16-byte piece of the output (PPT = 1), or, for large plans,
+// per PPT = 4 pieces of one row in consecutive fragments, so the row lookup
+// and the index arithmetic are paid once per four (the Philox rounds stay
+// one block per four elements).  Consecutive threads write consecutive
+// bytes; the source row piece is gathered from h (L2-resident).
 // =====================================================================
-template <bool BF16>
+// Pieces from which the launch gives each thread four of them: at the
+// batched 70B (2^20.3 pieces, 1280 blocks) the masking took 14.7 against
+// 18.0 us; at the 60-node tree (2^18.3 pieces, 320 blocks, too few to hide
+// latency) 9.1 against 7.8 us, so that plan keeps one piece per thread.
+constexpr size_t kPrepFourMin = (size_t)1 << 19;
+
+template <bool BF16, int PPT>
 __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* __restrict__ h, void* __restrict__ Hm,
                                                      RowMeta* __restrict__ meta, uint32_t* __restrict__ dbg_mask) {
     constexpr int esz = BF16 ? 2 : 4;
     constexpr int EPP = 16 / esz;  // elements per 16-byte piece
-    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t n16 = (size_t)P.R_phys * P.nkb * 4;
-    if (q >= n16) return;
-    const int lane = (int)(q & 63);
-    // (tile * nkb + kb) * msub + m: at most R_phys * nkb / 16 fragments, far
+    const size_t qt = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const uint32_t msub = (uint32_t)P.msub, nkq = (uint32_t)(P.nkb / PPT);
+    if (qt >= (size_t)P.R_phys * nkq * 4) return;
+    const int lane = (int)(qt & 63);
+    // (tile * nkq + kq) * msub + m: at most R_phys * nkb / 16 fragments, far
     // below 2^32, so the index splits in 32-bit arithmetic
-    const uint32_t frag = (uint32_t)(q >> 6);
-    const uint32_t msub = (uint32_t)P.msub, nkb = (uint32_t)P.nkb;
+    const uint32_t frag = (uint32_t)(qt >> 6);
     const uint32_t tk = frag / msub;
     const int m = (int)(frag - tk * msub);
-    const uint32_t tile_u = tk / nkb;
-    const int kb = (int)(tk - tile_u * nkb);
+    const uint32_t tile_u = tk / nkq;
+    const int kb0 = (int)(tk - tile_u * nkq) * PPT;  // this thread's first fragment
     const int tile = (int)tile_u;
     const int r = 16 * m + (lane & 15);
     const int rho = tile * P.MT + r;
-    const int o = kb * 64 + (lane >> 4) * 16;  // byte offset within the row
-    const int e0 = o / esz;                   // first element of the piece
     const RowInfo ri = row_info(P, rho);
-    if (kb == 0 && (lane >> 4) == 0) {
+    if (kb0 == 0 && (lane >> 4) == 0) {
         RowMeta mt;
         const bool valid = ri.b >= 0;
         mt.canon = valid ? (ri.b * P.T1 + ri.t) * P.K + ri.i : -1;
@@ -146,39 +152,48 @@ __global__ __launch_bounds__(256) void k_prep_packed(const Plan P, const void* _
         mt.inv_k = valid && ri.lossy ? seq_inv_k(P, ri.b) : 0.0f;
         meta[rho] = mt;
     }
-    uint32_t bits = 0u;  // bit k: keep element e0 + k
-    if (ri.b >= 0) {
-        if (ri.lossy) {
-            const uint32_t pidx = (uint32_t)(ri.b * P.T1 + ri.t);
-            const uint32_t thr = seq_thresh(P, ri.b);
+    const uint32_t pidx = ri.b >= 0 ? (uint32_t)(ri.b * P.T1 + ri.t) : 0u;
+    const uint32_t thr = ri.b >= 0 && ri.lossy ? seq_thresh(P, ri.b) : 0u;
+    const uint8_t* hrow = (const uint8_t*)h + ((size_t)pidx * P.d) * esz;
 #pragma unroll
-            for (int qq = 0; qq < EPP / 4; ++qq) {
-                const u32x4 rr =
-                    philox10(u32x4{(uint32_t)(e0 / 4 + qq), pidx, (uint32_t)ri.i, kStreamMask}, P.key0, P.key1);
-                bits |= (uint32_t)(rr.x >= thr) << (4 * qq);
-                bits |= (uint32_t)(rr.y >= thr) << (4 * qq + 1);
-                bits |= (uint32_t)(rr.z >= thr) << (4 * qq + 2);
-                bits |= (uint32_t)(rr.w >= thr) << (4 * qq + 3);
+    for (int j = 0; j < PPT; ++j) {
+        const int kb = kb0 + j;
+        const int o = kb * 64 + (lane >> 4) * 16;  // byte offset within the row
+        const int e0 = o / esz;                   // first element of the piece
+        uint32_t bits = 0u;                       // bit k: keep element e0 + k
+        if (ri.b >= 0) {
+            if (ri.lossy) {
+#pragma unroll
+                for (int qq = 0; qq < EPP / 4; ++qq) {
+                    const u32x4 rr = philox10(u32x4{(uint32_t)(e0 / 4 + qq), pidx, (uint32_t)ri.i, kStreamMask},
+                                              P.key0, P.key1);
+                    bits |= (uint32_t)(rr.x >= thr) << (4 * qq);
+                    bits |= (uint32_t)(rr.y >= thr) << (4 * qq + 1);
+                    bits |= (uint32_t)(rr.z >= thr) << (4 * qq + 2);
+                    bits |= (uint32_t)(rr.w >= thr) << (4 * qq + 3);
+                }
+            } else {
+                bits = (1u << EPP) - 1u;
+            }
+        }
+        v4u x = v4u{0, 0, 0, 0};
+        if (ri.b >= 0) x = *(const v4u*)(hrow + o);
+        if (BF16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = (bits >> (2 * k)) & 1u, hi = (bits >> (2 * k + 1)) & 1u;
+                x[k] = (lo ? (x[k] & 0x0000ffffu) : 0u) | (hi ? (x[k] & 0xffff0000u) : 0u);
             }
         } else {
-            bits = (1u << EPP) - 1u;
-        }
-    }
-    v4u x = v4u{0, 0, 0, 0};
-    if (ri.b >= 0) x = *(const v4u*)((const uint8_t*)h + ((size_t)(ri.b * P.T1 + ri.t) * P.d) * esz + o);
-    if (BF16) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = (bits >> (2 * k)) & 1u, hi = (bits >> (2 * k + 1)) & 1u;
-            x[k] = (lo ? (x[k] & 0x0000ffffu) : 0u) | (hi ? (x[k] & 0xffff0000u) : 0u);
+            for (int k = 0; k < 4; ++k) x[k] = ((bits >> k) & 1u) ? x[k] : 0u;
         }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = ((bits >> k) & 1u) ? x[k] : 0u;
+        const size_t q = (((size_t)tile * P.nkb + kb) * msub + m) * 64 + lane;  // consecutive lanes, consecutive pieces
+        *(v4u*)((uint8_t*)Hm + q * 16) = x;
+        if (dbg_mask && ri.b >= 0)  // keep bits of this piece into their mask word (the word starts zeroed)
+            atomicOr(&dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * (P.d >> 5) + (e0 >> 5)],
+                     bits << (e0 & 31));
     }
-    *(v4u*)((uint8_t*)Hm + q * 16) = x;
-    if (dbg_mask && ri.b >= 0)  // keep bits of this piece into their mask word (the word starts zeroed)
-        atomicOr(&dbg_mask[((size_t)(ri.b * P.T1 + ri.t) * P.K + ri.i) * (P.d >> 5) + (e0 >> 5)], bits << (e0 & 31));
 }
 
 // =====================================================================
@@ -2133,11 +2148,22 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {
 hipError_t launch_prep(const Plan& P, const void* h, void* Hm, RowMeta* meta, uint32_t* dbg_mask, hipStream_t st) {
     if (P.w_packed) {
         const size_t n16 = (size_t)P.R_phys * P.nkb * 4;
-        const dim3 grid((unsigned)((n16 + 255) / 256));
-        if (P.dtype == 1)
-            hipLaunchKernelGGL(k_prep_packed<true>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
-        else
-            hipLaunchKernelGGL(k_prep_packed<false>, grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+        // large plans: four consecutive pieces of a row per thread, so the
+        // row lookup and index arithmetic are paid once per four; small
+        // plans keep one piece per thread (latency: more threads in flight)
+        const bool four = P.nkb % 4 == 0 && n16 >= kPrepFourMin;
+        const dim3 grid((unsigned)(((four ? n16 / 4 : n16) + 255) / 256));
+        if (P.dtype == 1) {
+            if (four)
+                hipLaunchKernelGGL((k_prep_packed<true, 4>), grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+            else
+                hipLaunchKernelGGL((k_prep_packed<true, 1>), grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+        } else {
+            if (four)
+                hipLaunchKernelGGL((k_prep_packed<false, 4>), grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+            else
+                hipLaunchKernelGGL((k_prep_packed<false, 1>), grid, dim3(256), 0, st, P, h, Hm, meta, dbg_mask);
+        }
         return hipGetLastError();
     }
     const dim3 grid(P.R_phys, ((P.d >> 3) + 255) / 256);

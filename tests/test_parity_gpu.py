@@ -428,6 +428,20 @@ def test_tile_kernel_short_reductions(d):
         _check(w.W, w.h, w.draft, w.q_hat, np.full(B, wl.JS, np.uint8), K, 0.2, [3], layout=P.PANELS)
 
 
+@pytest.mark.parametrize("cfg,d", [(1, 4096), (0, 2048)], ids=["bf16", "fp32"])
+def test_packed_prep_four_pieces_per_thread(cfg, d):
+    """Panel-order plans of at least 2^19 operand pieces give each masking
+    thread four consecutive fragments of one row: 1104 rows of 4096 bf16 or
+    2048 fp32 elements, every rule, masks compared bit for bit.  The shapes
+    stay small in the vocabulary so the oracle is quick."""
+    B, gamma, K = 36, 7, 4
+    modes = np.array([wl.LOSSLESS] * 2 + [wl.NAIVE, wl.JS] * 17, np.uint8)
+    rows = int((modes != wl.LOSSLESS).sum()) * (gamma + 1) * K + int((modes == wl.LOSSLESS).sum()) * (gamma + 1)
+    assert rows * (d * (2 if cfg == 1 else 4) // 64) * 4 >= 1 << 19  # live rows alone pass the threshold
+    w = wl.generate(cfg, B=B, gamma=gamma, d=d, V=1000, K=K, planted=0.8)
+    _check(w.W, w.h, w.draft, w.q_hat, modes, K, 0.25, [5], layout=P.PANELS)
+
+
 def test_calls_on_one_handle_carry_no_state(layout):
     """Consecutive calls on one handle, each with a different set of lossless
     sequences (whose residual races meet in per-sequence workspace slots),
