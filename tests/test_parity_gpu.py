@@ -286,6 +286,30 @@ def test_maximum_batch_gamma_and_heads(layout):
     torch.cuda.synchronize()
 
 
+def test_race_chunks_capped_with_many_lossless_sequences(layout):
+    """256 lossless sequences over |V| = 20000: the planner's chunk for that
+    many races (5120 entries) is cut to the 4096 a race block covers, so each
+    sequence's race spans five blocks whose winners meet in its own slots;
+    every sequence compared."""
+    import torch
+
+    B, gamma, K = 256, 1, 1
+    w = wl.generate(2, B=B, gamma=gamma, d=64, V=20000, K=K, planted=0.6)
+    modes = np.full(B, wl.LOSSLESS, np.uint8)
+    ver = P.make_verifier(w.W, w.h, K)
+    inp = P.Inputs(w.W, w.h, w.draft, w.q_hat)
+    rep = P.Report()
+    for seed in (4, 11):
+        print(f"  B={B} lossless V=20000 seed={seed} layout={layout}", flush=True)
+        g = P.run_gpu(ver, inp, modes, K, 0.0, seed, layout=layout)
+        o = P.oracle_run(w.W, w.h, w.draft, w.q_hat, modes, K, 0.0, seed)
+        rep.add(P.compare(g, o, modes, K))
+    ver.close()
+    P.assert_caps(rep)
+    assert rep.sequences == 2 * B
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("d,V", [(65536, 1024), (64, 524288)], ids=["widest_hidden", "largest_vocab"])
 def test_widest_hidden_and_largest_vocabulary(d, V, layout):
     """The descriptor's limits on d and |V|, every rule."""
