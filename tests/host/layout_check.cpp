@@ -77,6 +77,9 @@ static void check_case(int d, int V, int maxB, int gamma, int kmax, int B, int K
           "js chunks\n");
     CHECK(nl == 0 || ((long long)P.race_chunks * P.race_chunk >= V && (long long)(P.race_chunks - 1) * P.race_chunk < V),
           "race chunks\n");
+    // a race block covers at most kRaceChunkMax entries in whole 1024-entry steps
+    CHECK(nl == 0 || (P.race_chunk <= kRaceChunkMax && P.race_chunk % 1024 == 0), "race chunk %d\n", P.race_chunk);
+    CHECK(sz.race >= (size_t)B * kRaceSlotStride * sizeof(unsigned long long), "race slots\n");
     CHECK(P.blk_js == P.n_js_pos * P.js_chunks && P.blk_race == nl * P.race_chunks, "block count\n");
     CHECK(gamma <= kMaxGamma && T1 <= 64, "gamma beyond one wave of positions\n");
     std::vector<int> seen((size_t)B * T1 * K, 0);
@@ -254,7 +257,8 @@ int main() {
         check_case(8192, 128256, 32, 7, 5, 32, 5, 0, wp);
         check_case(5120, 151936, 64, 5, 8, 64, 8, 2, wp);
         check_case(4096, 128256, 1, 7, 5, 1, 5, 0, wp);
-        cases += 3;
+        check_case(64, 20000, 256, 1, 1, 256, 1, 1, wp);  // many races: chunks cut to kRaceChunkMax
+        cases += 4;
     }
     for (int wp = 0; wp <= 1; ++wp)
         for (int K : {1, 3, 5, 8, 16})
